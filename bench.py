@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused tree-verify attention call on one MI355X.
+
+One step = one ``tree_attn_verify`` call (prefix pass + tree mask + suffix pass +
+merge, one kernel launch) over one batch of seeded synthetic input that is
+already resident in HBM.  Default workload: the Llama-3.1-8B-shaped verify step
+(bf16, batch 1, 32 query / 8 KV heads, head dim 128, 8192-token paged prefix,
+12-node tree).
+
+Timing protocol
+* The 256 MB last-level cache is larger than one batch (33.8 MB), so R
+  independent replicas of the inputs (each its own KV pool, block table, q, tree
+  K/V, >= 1 GiB together) are used in rotation; every step reads HBM.
+* W warm-up steps, then K timed steps queued back to back on one stream.  The
+  GPU is first held by a short spin kernel so that the host queues all K steps
+  before the first one starts; one pair of HIP events on the launch stream
+  brackets the K steps (events between steps would themselves cost several
+  microseconds at this scale).
+* ms_per_step = (end event - start event) / K.  With one kernel per step this is
+  the kernel's average duration plus the (sub-0.1 us) gap between queued
+  launches; value = algorithmic bytes / ms_per_step.
+* cpu_baseline: the fp64 NumPy oracle on the same workload, on this host.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify attention µs/call + achieved HBM GB/s (% of peak), 8k ctx"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_cfg2_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ancestor_pairs(parents) -> int:
+    """sum over nodes of |ancestor-or-self set| (for the flop count)."""
+    total = 0
+    par = [int(x) for x in parents]
+    for i in range(len(par)):
+        j = i
+        while j != -1:
+            total += 1
+            j = par[j]
+    return total
+
+
+def algorithmic_bytes(inp) -> int:
+    s = inp.elem_bytes
+    Hq, Hkv, D = inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    tot = 0
+    for b in range(inp.batch):
+        P = int(inp.prefix_lens[b])
+        T = int(inp.tree_offsets[b + 1] - inp.tree_offsets[b])
+        tot += (2 * P * Hkv * D * s + T * Hq * D * s + 2 * T * Hkv * D * s + T * Hq * D * s
+                + 4 * T * Hq + 4 * math.ceil(P / 64) + 4 * T + 8)
+    return tot
+
+
+def algorithmic_flops(inp) -> int:
+    Hq, D = inp.num_q_heads, inp.head_dim
+    tot = 0
+    for b in range(inp.batch):
+        lo, hi = int(inp.tree_offsets[b]), int(inp.tree_offsets[b + 1])
+        P = int(inp.prefix_lens[b])
+        tot += 4 * Hq * D * ((hi - lo) * P + ancestor_pairs(inp.parents[lo:hi]))
+    return tot
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_attention_verify_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_index: int, split: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources and the same workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    if rec.get("config") != config_index or rec.get("split_tokens") != split:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float, nbytes: int):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify(inp)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    per = el / calls
+    return {
+        "value": nbytes / per / 1e9,
+        "unit": "GB/s",
+        "us_per_call": per * 1e6,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{calls} full fp64 oracle verify call(s) of the benchmark workload "
+                  f"({el:.1f} s of CPU time)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--entry", choices=("verify", "split"), default="verify",
+                    help="fused single launch (default) or the four-call split path")
+    ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py is single-process; WORLD_SIZE > 1 is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tree_attention_verify_attn_amd as ta
+    from tree_attention_verify_attn_amd._lib import load
+    from workloads import CONFIG_NAMES, make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    lib = load()
+
+    log(f"building workload cfg{args.config}")
+    inp = make_config(args.config)
+    nbytes = algorithmic_bytes(inp)
+    flops = algorithmic_flops(inp)
+    dt = ta.DTYPE_BF16 if inp.dtype == "bf16" else ta.DTYPE_F32
+    shape = ta.make_shape(batch=inp.batch, num_q_heads=inp.num_q_heads,
+                          num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                          max_blocks_per_seq=inp.max_blocks_per_seq,
+                          max_tree_nodes=inp.max_tree_nodes, max_prefix_len=inp.max_prefix_len,
+                          total_tree_nodes=inp.total_tree_nodes, num_blocks=inp.num_blocks,
+                          dtype=dt, softmax_scale=inp.softmax_scale,
+                          split_tokens=args.split_tokens)
+    split = ta.split_tokens(shape)
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    host_arrays = [inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.prefix_lens,
+                   inp.k_tree, inp.v_tree, inp.parents, inp.tree_offsets]
+    footprint = sum(a.nbytes for a in host_arrays)
+    R = max(1, math.ceil(args.replica_bytes / footprint))
+    log(f"footprint {footprint / 1e6:.1f} MB -> {R} replicas; split_tokens {split}")
+    first = [dev(a) for a in host_arrays]
+    replicas = [first] + [[t.clone() for t in first] for _ in range(R - 1)]
+    ws = ta.alloc_workspace(shape)
+    N, Hq, D = inp.total_tree_nodes, inp.num_q_heads, inp.head_dim
+    outs = [torch.empty(N, Hq, D, dtype=first[0].dtype, device="cuda") for _ in range(R)]
+    lses = [torch.empty(N, Hq, dtype=torch.float32, device="cuda") for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    wsp, wsn = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    call_args = []
+    for r in range(R):
+        q, kc, vc, bt, pl, kt, vt, par, off = replicas[r]
+        call_args.append((ctypes.byref(shape), q.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                          bt.data_ptr(), pl.data_ptr(), kt.data_ptr(), vt.data_ptr(),
+                          par.data_ptr(), off.data_ptr(), outs[r].data_ptr(),
+                          lses[r].data_ptr(), wsp, wsn, sh))
+    verify = lib.tree_attn_verify
+
+    if args.entry == "verify":
+        def step(r):
+            rc = verify(*call_args[r])
+            if rc:
+                raise RuntimeError(f"tree_attn_verify: {ta.status_string(rc)}")
+    else:
+        # split path: mask build + prefix pass + suffix pass + merge, four launches
+        masks = torch.empty(N, dtype=torch.int64, device="cuda")
+        po = torch.empty(N, Hq, D, dtype=torch.float32, device="cuda")
+        pl = torch.empty(N, Hq, dtype=torch.float32, device="cuda")
+        so = torch.empty_like(po)
+        sl = torch.empty_like(pl)
+        sp = ctypes.byref(shape)
+
+        def step(r):
+            q, kc, vc, bt, pl_, kt, vt, par, off = replicas[r]
+            rc = lib.tree_attn_build_mask(sp, par.data_ptr(), off.data_ptr(), masks.data_ptr(),
+                                          wsp, wsn, sh)
+            rc = rc or lib.tree_attn_prefix(sp, q.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                            bt.data_ptr(), pl_.data_ptr(), off.data_ptr(),
+                                            po.data_ptr(), pl.data_ptr(), wsp, wsn, sh)
+            rc = rc or lib.tree_attn_suffix(sp, q.data_ptr(), kt.data_ptr(), vt.data_ptr(),
+                                            masks.data_ptr(), off.data_ptr(), so.data_ptr(),
+                                            sl.data_ptr(), sh)
+            rc = rc or lib.tree_attn_merge(N * Hq, D, int(shape.dtype), po.data_ptr(),
+                                           pl.data_ptr(), so.data_ptr(), sl.data_ptr(),
+                                           outs[r].data_ptr(), lses[r].data_ptr(), sh)
+            if rc:
+                raise RuntimeError(f"split path: {ta.status_string(rc)}")
+
+    # correctness spot check of the benchmarked call itself
+    step(0)
+    torch.cuda.synchronize()
+    err = ta.get_error(ws)
+    if err != 0:
+        raise RuntimeError(f"device error {ta.status_string(err)}")
+
+    log(f"warm-up {args.warmup}")
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    # hold the GPU long enough for the host to queue every timed step
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    torch.cuda._sleep(1_000_000)
+    s1.record()
+    torch.cuda.synchronize()
+    per_cycle_ms = max(s0.elapsed_time(s1), 1e-3) / 1_000_000
+    hold_ms = 20.0 + 0.1 * args.steps
+    cycles = int(hold_ms / per_cycle_ms)
+
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {K} steps ({args.entry})")
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    torch.cuda._sleep(cycles)
+    e0.record()
+    for i in range(K):
+        step(i % R)
+    e1.record()
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / K
+    kernel_ms = ms_per_step
+    err = ta.get_error(ws)
+    if err != 0:
+        raise RuntimeError(f"device error during timing: {ta.status_string(err)}")
+
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.config, split)
+    result = {
+        "metric": METRIC,
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "entry": args.entry,
+        "pct_of_peak_hbm": round(100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(inp.total_tree_nodes / (ms_per_step * 1e-3), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[args.config],
+            "batch": inp.batch,
+            "num_q_heads": inp.num_q_heads,
+            "num_kv_heads": inp.num_kv_heads,
+            "head_dim": inp.head_dim,
+            "prefix_tokens": int(inp.prefix_lens.sum()),
+            "tree_nodes": inp.total_tree_nodes,
+            "split_tokens": split,
+            "replicas": R,
+            "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": ("attn_kernel<bf16,128,fused> (tree_attn_verify)" if args.entry == "verify"
+                       else "split path: mask + prefix + suffix + merge kernels"),
+            "mfma_util": round(flops / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+        },
+        "host_wall_s": round(t_host, 3),
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, nbytes)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,189 @@
+/*
+ * tree_attn.h - C ABI of the MI355X (gfx950) split tree-verify attention library
+ * (libtreeattn.so).
+ *
+ * What it computes.  In the verify step of tree speculative decoding the draft
+ * tree's tokens are flattened into one sequence after the committed prefix.
+ * Each tree token's attention is computed in two pieces: one over the committed
+ * prefix, which needs no custom mask, and one among the tree tokens, which
+ * needs the tree mask.  The two partial results are combined exactly by their
+ * log-sum-exp (merge_attentions).  [pith.science review of arXiv 2508.08192,
+ * "What carries the argument"; the merge of attention over disjoint KV chunks
+ * is credited to Hydragen (Juravsky et al. 2024) in the pith.science verdict
+ * record, pith_extraction.supporting_citations]
+ *
+ * Readings of what the pages leave open (all fixed here, for every call):
+ *   - tree mask = ancestor-or-self: tree node i attends to tree node j iff j is
+ *     i or an ancestor of i (SpecInfer tree verification);
+ *   - every tree node attends to all prefix_lens[b] prefix tokens;
+ *   - grouped-query attention: query head h reads KV head h / G, G = Hq / Hkv;
+ *   - scores s = softmax_scale * dot(q, k), no positional encoding applied;
+ *   - lse outputs are natural logarithms; a row with no visible key gets
+ *     o = 0 and lse = -inf.
+ *
+ * Conventions shared by every entry point.
+ *   - Every pointer argument except `shape` is a DEVICE pointer owned by the
+ *     caller.  The library never allocates or frees device memory and never
+ *     synchronises, except tree_attn_get_error (documented below).  All calls
+ *     are asynchronous on `stream` and safe to capture in a HIP graph.
+ *   - All tensors are dense, row-major, contiguous, at least 16-byte aligned.
+ *   - Element type of q, k_cache, v_cache, k_tree, v_tree and `out` is
+ *     shape->dtype (bf16 = raw 16-bit patterns, or fp32).  Partial outputs
+ *     (o_prefix, o_suffix, lse_*) are fp32.
+ *   - Layouts (N = total_tree_nodes, Hq, Hkv, D = head_dim, 64-token blocks):
+ *       q, out            [N, Hq, D]
+ *       lse_out, lse_*    [N, Hq]            fp32
+ *       o_prefix, o_suffix[N, Hq, D]         fp32
+ *       k_cache, v_cache  [num_blocks, Hkv, 64, D]
+ *       block_table       int32 [batch, max_blocks_per_seq]; token t of
+ *                         sequence b is slot t % 64 of block block_table[b][t/64]
+ *                         (PagedAttention layout, Kwon et al. 2023, named in the
+ *                         same supporting_citations field as the scheme adapted
+ *                         for tree attention)
+ *       prefix_lens       int32 [batch]
+ *       k_tree, v_tree    [N, Hkv, D]
+ *       parents           int32 [N]; local index of the parent inside its own
+ *                         sequence's tree, -1 for a root, parent[i] < i
+ *       tree_offsets      int32 [batch + 1]; tree of sequence b is rows
+ *                         [tree_offsets[b], tree_offsets[b+1]); tree_offsets[0]
+ *                         = 0 and tree_offsets[batch] = N
+ *       mask              uint64 [N]; bit j of mask[tree_offsets[b] + i] set
+ *                         iff local node j is i or an ancestor of i
+ *   - Return codes report what the host can see: bad scalars, null or
+ *     misaligned pointers, unsupported shapes, a workspace that is too small,
+ *     launch failures.  Properties of device data (a bad parent array, a prefix
+ *     length beyond max_prefix_len, a block id outside [0, num_blocks), bad
+ *     tree_offsets) are checked by the kernels, which never read out of bounds
+ *     because of them; they set a flag in the workspace that
+ *     tree_attn_get_error reports.  Outputs of an affected sequence are then
+ *     unspecified.
+ *   - Thread safety: calls may come from any host thread.  Calls that run
+ *     concurrently (different streams) must use different workspaces.
+ */
+#ifndef TREE_ATTN_H_
+#define TREE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TA_OK = 0,
+  TA_ERR_INVALID_ARG = 1,  /* bad scalar, null or misaligned pointer */
+  TA_ERR_UNSUPPORTED = 2,  /* shape outside what the kernels implement */
+  TA_ERR_BAD_TREE = 3,     /* device-detected: parent array or tree_offsets invalid */
+  TA_ERR_WORKSPACE = 4,    /* workspace null or smaller than tree_attn_workspace_size */
+  TA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
+  TA_ERR_BAD_PREFIX = 6,   /* device-detected: prefix length or block id out of range */
+  TA_ERR_TIMEOUT = 7,      /* device-detected: a bounded cross-workgroup wait gave up */
+  TA_ERR_PLACEMENT = 8     /* device-detected: a workgroup ran on another XCD than the
+                              round-robin placement the work split relies on */
+} ta_status;
+
+typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
+
+/* Host-side description of one call.  Everything here is a host value; the
+ * per-sequence data (prefix lengths, trees) stays on the device. */
+typedef struct {
+  int32_t batch;              /* B >= 1 (B <= 4096) */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* D in {64, 128} */
+  int32_t block_size;         /* tokens per KV block; must be 64 */
+  int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
+  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size, 1..64 */
+  int32_t max_prefix_len;     /* upper bound on prefix_lens[b], 0..64*max_blocks_per_seq */
+  int32_t total_tree_nodes;   /* N = tree_offsets[B] */
+  int32_t num_blocks;         /* pool size: valid block ids are [0, num_blocks) */
+  int32_t split_tokens;       /* prefix tokens per work item: 0 = library heuristic,
+                                 else a positive multiple of 64 */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim) */
+  ta_dtype dtype;             /* element type of q, caches, tree K/V and out */
+} ta_shape;
+
+/* Bytes of device workspace tree_attn_prefix / tree_attn_verify /
+ * tree_attn_build_mask need for `shape` (0 if the shape is invalid).
+ * A workspace must be zero-filled before its first use (tree_attn_workspace_init
+ * does that); every call that returns TA_OK leaves its counters zeroed again,
+ * so the same workspace can be reused call after call on one stream. */
+size_t tree_attn_workspace_size(const ta_shape* shape);
+
+/* Zero-fill a workspace with a kernel (no hipMemset, so graph capture is safe). */
+ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Build the ancestor-or-self mask words of every tree:
+ * mask[i] = (parent[i] < 0 ? 0 : mask[parent[i]]) | (1 << i), per sequence.
+ * Validates each parent (-1 or an earlier node of the same tree) and each tree
+ * size (1..max_tree_nodes); a violation raises TA_ERR_BAD_TREE in the
+ * workspace flag and that tree's words are zero.
+ * [pith.science review, "What carries the argument": the draft-token piece
+ * "needs the tree mask"] */
+ta_status tree_attn_build_mask(const ta_shape* shape, const int32_t* parents,
+                               const int32_t* tree_offsets, uint64_t* mask_out,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Prefix pass: attention of every tree query over its sequence's whole
+ * committed prefix (no mask), read through the block table.  Writes the
+ * normalised output o_prefix and lse_prefix (fp32).  A sequence with
+ * prefix_lens[b] == 0 gets o = 0, lse = -inf.
+ * [pith.science review, "What carries the argument": query-to-prefix piece] */
+ta_status tree_attn_prefix(const ta_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* prefix_lens, const int32_t* tree_offsets,
+                           float* o_prefix, float* lse_prefix, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Suffix pass: attention of every tree query over the tree tokens whose bit is
+ * set in its mask word (normally from tree_attn_build_mask).  Bits at or above
+ * the tree size are ignored.  Writes o_suffix, lse_suffix (fp32).
+ * [pith.science review, "What carries the argument": draft-token piece] */
+ta_status tree_attn_suffix(const ta_shape* shape, const void* q, const void* k_tree,
+                           const void* v_tree, const uint64_t* mask,
+                           const int32_t* tree_offsets, float* o_suffix, float* lse_suffix,
+                           hipStream_t stream);
+
+/* merge_attentions for two results over disjoint key sets, row by row:
+ * lse = log(exp(lse_a) + exp(lse_b)),
+ * out = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b.
+ * rows = N * Hq; o_* are fp32 [rows, head_dim]; out is out_dtype; lse_out fp32.
+ * Both inputs -inf gives out = 0, lse = -inf.  `out` may alias o_a only when
+ * out_dtype is fp32.
+ * [pith.science verdict record, pith_extraction.supporting_citations, Juravsky
+ * et al. 2024] */
+ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype,
+                          const float* o_a, const float* lse_a, const float* o_b,
+                          const float* lse_b, void* out, float* lse_out,
+                          hipStream_t stream);
+
+/* Fused verify: prefix pass + mask build + suffix pass + merge in one kernel
+ * launch.  Writes out (shape->dtype) and lse_out (fp32, may be NULL).
+ * [pith.science review, "What carries the argument"] */
+ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* prefix_lens, const void* k_tree,
+                           const void* v_tree, const int32_t* parents,
+                           const int32_t* tree_offsets, void* out, float* lse_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, reads and clears the device error flag of workspace
+ * `ws` and returns it (TA_OK if no kernel flagged anything).  This is the only
+ * entry point that blocks the host. */
+ta_status tree_attn_get_error(void* ws, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* tree_attn_status_string(ta_status status);
+
+/* Work-item size (prefix tokens per work item) the library would use for
+ * `shape`; 0 if the shape is invalid.  For inspection and benchmarking. */
+int32_t tree_attn_split_tokens(const ta_shape* shape);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H_ */

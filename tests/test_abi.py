@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad host arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verify_attn_amd as ta
+from tree_attention_verify_attn_amd._lib import EXPORTED, Shape, load
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+FAKE = 0x100000  # aligned non-null address; never dereferenced on these paths
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(tree_attn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(EXPORTED) == header_functions()
+
+
+def test_library_exports_every_header_symbol():
+    lib = load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_shape_struct_layout_matches_header():
+    # 11 int32, one float, one enum (int32) -> 13 * 4 bytes
+    assert ctypes.sizeof(Shape) == 52
+
+
+def shape(**kw):
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_blocks_per_seq=128,
+                max_tree_nodes=12, max_prefix_len=8192, total_tree_nodes=12, num_blocks=128,
+                dtype=ta.DTYPE_BF16)
+    base.update(kw)
+    return ta.make_shape(**base)
+
+
+def test_workspace_size_valid_and_monotone():
+    a = ta.workspace_size(shape(split_tokens=256))
+    b = ta.workspace_size(shape(split_tokens=256, max_prefix_len=4096))
+    c = ta.workspace_size(shape(split_tokens=256, batch=2, max_prefix_len=8192))
+    assert a > 0 and b > 0 and c > 0
+    assert b < a < c
+
+
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(max_tree_nodes=65),
+    dict(batch=5000),
+])
+def test_unsupported_shapes(kw):
+    s = shape(**kw)
+    assert ta.workspace_size(s) == 0
+    rc = load().tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None)
+    assert rc == 2  # TA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(num_q_heads=30), dict(batch=0), dict(num_kv_heads=0), dict(max_tree_nodes=0),
+    dict(max_prefix_len=-1), dict(max_prefix_len=128 * 64 + 1), dict(split_tokens=100),
+    dict(dtype=7), dict(num_blocks=0), dict(max_blocks_per_seq=0),
+])
+def test_invalid_shapes(kw):
+    s = shape(**kw)
+    assert ta.workspace_size(s) == 0
+    rc = load().tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None)
+    assert rc == 1  # TA_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers():
+    s = shape()
+    lib = load()
+    args = [FAKE] * 11
+    for i in range(11):
+        bad = list(args)
+        bad[i] = None
+        if i == 10:   # lse_out may be null; block_table is index 3
+            continue
+        assert lib.tree_attn_verify(ctypes.byref(s), *bad, FAKE, 1 << 40, None) == 1, i
+    mis = list(args)
+    mis[0] = FAKE + 2
+    assert lib.tree_attn_verify(ctypes.byref(s), *mis, FAKE, 1 << 40, None) == 1
+
+
+def test_workspace_checks():
+    s = shape()
+    lib = load()
+    need = ta.workspace_size(s)
+    assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), FAKE, need - 1, None) == 4
+    assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), None, need, None) == 4
+    assert lib.tree_attn_prefix(ctypes.byref(s), *([FAKE] * 8), FAKE + 8, need, None) == 4
+
+
+def test_merge_argument_checks():
+    lib = load()
+    assert lib.tree_attn_merge(-1, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.tree_attn_merge(4, 126, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.tree_attn_merge(4, 128, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.tree_attn_merge(0, 128, 0, None, None, None, None, None, None, None) == 0
+
+
+def test_status_strings():
+    for code in range(9):
+        assert ta.status_string(code) and ta.status_string(code) != "unknown status"
+    assert ta.status_string(99) == "unknown status"
+
+
+def test_split_tokens_bounds():
+    for kw in [dict(), dict(batch=256), dict(max_prefix_len=32768, max_blocks_per_seq=512),
+               dict(split_tokens=64, max_prefix_len=32768, max_blocks_per_seq=512)]:
+        s = shape(**kw)
+        c = ta.split_tokens(s)
+        assert c % 64 == 0 and 64 <= c <= 4096
+        assert -(-s.max_prefix_len // c) <= 64    # at most 64 chunks per prefix

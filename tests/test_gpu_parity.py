@@ -1,0 +1,290 @@
+"""GPU parity: every entry point of the HIP library against the fp64 oracle.
+
+Tolerances (from the numerics of the path): fp32 inputs max |o err| 1e-5; bf16
+inputs max |o err| 2e-2 and max |lse err| 1e-3; mask words bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_close, assert_close_lse, host, run_split, run_verify, say,
+                      to_device, tolerances)
+from helpers import random_tree, read_mask_table, small_inputs
+from workloads import TREE_12, make_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_verify(inp, out, lse, what):
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    err = assert_close(host(out), o_want, tol_o, f"{what} o")
+    assert_close_lse(host(lse), l_want, tol_l, f"{what} lse")
+    return err
+
+
+# ------------------------------------------------------------------ mask
+def test_mask_golden_tables_bit_exact():
+    import tree_attention_verify_attn_amd as ta
+    table = read_mask_table()
+    trees = [par for _, par, _ in table]
+    inp = small_inputs(1, B=len(trees), D=64, trees=trees, prefix_lens=[1] * len(trees))
+    d = to_device(inp)
+    say("mask golden tables")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    got = mask.cpu().numpy().view(np.uint64)
+    want = np.concatenate([np.array(w, dtype=np.uint64) for _, _, w in table])
+    np.testing.assert_array_equal(got, want)
+    assert ta.get_error(d.workspace) == 0
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mask_random_trees_bit_exact(seed):
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(50 + seed)
+    trees = [random_tree(rng, int(rng.integers(1, 65)), forest_p=0.05) for _ in range(40)]
+    trees.append([-1] + list(range(63)))  # 64-node chain
+    inp = small_inputs(seed, B=len(trees), D=64, trees=trees, prefix_lens=[0] * len(trees))
+    d = to_device(inp)
+    say(f"mask random trees seed {seed}")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64), oracle.build_masks(inp))
+
+
+def test_mask_flags_bad_parents():
+    import tree_attention_verify_attn_amd as ta
+    trees = [[-1, 0, 1], [-1, 2, 0], [-1, 0]]   # the middle tree has a forward parent
+    inp = small_inputs(2, B=3, D=64, trees=trees, prefix_lens=[0, 0, 0])
+    d = to_device(inp)
+    say("mask bad parents")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 3          # TA_ERR_BAD_TREE
+    got = mask.cpu().numpy().view(np.uint64)
+    np.testing.assert_array_equal(got[:3], oracle.ancestor_or_self_mask([-1, 0, 1]))
+    np.testing.assert_array_equal(got[3:6], 0)     # bad tree -> zero words
+    np.testing.assert_array_equal(got[6:], oracle.ancestor_or_self_mask([-1, 0]))
+    assert ta.get_error(d.workspace) == 0          # flag cleared by the read
+
+
+# ----------------------------------------------------------------- merge
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_merge_vs_oracle(out_dtype):
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(60)
+    rows, D = 777, 128
+    oa, ob = rng.standard_normal((rows, D)), rng.standard_normal((rows, D))
+    la, lb = rng.standard_normal(rows) * 5, rng.standard_normal(rows) * 5
+    la[::7] = -np.inf
+    lb[::11] = -np.inf
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+    say(f"merge out_dtype {out_dtype}")
+    out, lse = ta.merge(t(oa), t(la), t(ob), t(lb), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    # the oracle merges the fp32-rounded inputs
+    r32 = lambda x: x.astype(np.float32).astype(np.float64)
+    wo, wl = oracle.merge(r32(oa), r32(la), r32(ob), r32(lb))
+    assert_close(host(out), wo, 1e-5 if out_dtype == 0 else 2e-2, "merge o")
+    assert_close_lse(host(lse), wl, 1e-5, "merge lse")
+
+
+# --------------------------------------------------------- prefix, suffix
+PIECE_CASES = [
+    ("cfg1", lambda: make_config(1)),
+    ("cfg2", lambda: make_config(2)),
+    ("cfg3", lambda: make_config(3)),
+    ("cfg4", lambda: make_config(4)),
+    ("cfg5-b24", lambda: make_config(5, batch_override=24)),
+    ("small-f32", lambda: small_inputs(70, dtype="f32", B=3, Hq=6, Hkv=2, D=64,
+                                       prefix_lens=(0, 200, 63))),
+    ("small-bf16", lambda: small_inputs(71, dtype="bf16", B=3, Hq=8, Hkv=1, D=128,
+                                        prefix_lens=(1, 129, 640))),
+]
+
+
+@pytest.mark.parametrize("name,make", PIECE_CASES, ids=[c[0] for c in PIECE_CASES])
+def test_split_path_pieces(name, make):
+    inp = make()
+    d = to_device(inp)
+    say(f"split path {name}")
+    out, lse, (po, pl, so, sl, mask) = run_split(d)
+    tol_o, tol_l = tolerances(inp)
+    np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64), oracle.build_masks(inp))
+    wpo, wpl = oracle.prefix_only(inp)
+    wso, wsl = oracle.suffix_only(inp)
+    # partial outputs are fp32; their error budget is the same as the final one
+    assert_close(host(po), wpo, tol_o, f"{name} prefix o")
+    assert_close_lse(host(pl), wpl, tol_l, f"{name} prefix lse")
+    assert_close(host(so), wso, tol_o, f"{name} suffix o")
+    assert_close_lse(host(sl), wsl, tol_l, f"{name} suffix lse")
+    _check_verify(inp, out, lse, f"{name} split")
+
+
+# ----------------------------------------------------------------- verify
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_verify_configs(idx):
+    inp = make_config(idx)
+    d = to_device(inp)
+    say(f"verify cfg{idx} split_tokens={d.shape.split_tokens}")
+    out, lse = run_verify(d)
+    import tree_attention_verify_attn_amd as ta
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, f"cfg{idx}")
+
+
+def test_verify_cfg5_full_size_sampled():
+    inp = make_config(5)
+    d = to_device(inp)
+    say("verify cfg5 full size")
+    out, lse = run_verify(d)
+    import tree_attention_verify_attn_amd as ta
+    assert ta.get_error(d.workspace) == 0
+    o, l = host(out), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    rng = np.random.default_rng(5)
+    N, Hq = inp.total_tree_nodes, inp.num_q_heads
+    # longest, shortest and random rows
+    seq_of = np.searchsorted(inp.tree_offsets, np.arange(N), side="right") - 1
+    P = inp.prefix_lens[seq_of]
+    picks = [int(np.argmax(P)), int(np.argmin(P)), N - 1, 0] + list(rng.integers(0, N, 60))
+    rows = [(n, int(rng.integers(0, Hq))) for n in picks]
+    wo, wl = oracle.verify_rows(inp, rows)
+    for k, (n, h) in enumerate(rows):
+        assert np.max(np.abs(o[n, h] - wo[k])) <= 2e-2, (n, h)
+        assert abs(l[n, h] - wl[k]) <= 1e-3, (n, h)
+
+
+@pytest.mark.parametrize("split", [64, 128, 256, 1024, 4096])
+def test_verify_split_sizes(split):
+    inp = make_config(4)
+    d = to_device(inp, split_tokens=split)
+    say(f"verify cfg4 split_tokens={split}")
+    out, lse = run_verify(d)
+    _check_verify(inp, out, lse, f"cfg4 split {split}")
+
+
+EDGE_CASES = [
+    ("empty-prefix", lambda: small_inputs(80, dtype="bf16", B=3, Hq=4, Hkv=2, D=128,
+                                          prefix_lens=(0, 0, 0))),
+    ("mixed-empty", lambda: small_inputs(81, dtype="bf16", B=4, Hq=8, Hkv=2, D=128,
+                                         prefix_lens=(0, 65, 1, 3000))),
+    ("single-node", lambda: small_inputs(82, dtype="bf16", B=2, Hq=4, Hkv=4, D=128,
+                                         prefix_lens=(100, 7), trees=[[-1], [-1]])),
+    ("chain64-G1", lambda: small_inputs(83, dtype="bf16", B=1, Hq=2, Hkv=2, D=128,
+                                        prefix_lens=(333,), trees=[[-1] + list(range(63))])),
+    ("rows>64-G8", lambda: small_inputs(84, dtype="bf16", B=2, Hq=8, Hkv=1, D=128,
+                                        prefix_lens=(513, 77), trees=[TREE_12, [-1, 0, 0]])),
+    ("rows=512", lambda: small_inputs(85, dtype="bf16", B=1, Hq=8, Hkv=1, D=128,
+                                      prefix_lens=(200,), trees=[[-1] + list(range(63))])),
+    ("d64-bf16", lambda: small_inputs(86, dtype="bf16", B=2, Hq=4, Hkv=2, D=64,
+                                      prefix_lens=(190, 64))),
+    ("d128-f32", lambda: small_inputs(87, dtype="f32", B=2, Hq=4, Hkv=1, D=128,
+                                      prefix_lens=(190, 1000))),
+    ("forest", lambda: small_inputs(88, dtype="bf16", B=1, Hq=4, Hkv=1, D=128,
+                                    prefix_lens=(90,), trees=[[-1, -1, 0, 1, -1]])),
+    ("keys-x4", lambda: small_inputs(89, dtype="bf16", B=2, Hq=5, Hkv=1, D=128,
+                                     prefix_lens=(700, 2), key_scale=4.0)),
+]
+
+
+@pytest.mark.parametrize("name,make", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_verify_edge_cases(name, make):
+    inp = make()
+    d = to_device(inp)
+    say(f"verify edge {name}")
+    out, lse = run_verify(d)
+    import tree_attention_verify_attn_amd as ta
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, name)
+
+
+def test_verify_workspace_reuse_and_determinism():
+    import tree_attention_verify_attn_amd as ta
+    inp = make_config(2)
+    d = to_device(inp)
+    say("verify cfg2 repeated calls")
+    out1, lse1 = run_verify(d)
+    out2, lse2 = run_verify(d)
+    out3, lse3 = run_verify(d)
+    assert torch.equal(out1, out2) and torch.equal(out2, out3)
+    assert torch.equal(lse1, lse2) and torch.equal(lse2, lse3)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out3, lse3, "cfg2 third call")
+
+
+def test_verify_block_permutation_bit_identical():
+    inp = make_config(3, batch_override=8)
+    d = to_device(inp)
+    say("verify block permutation A")
+    out_a, lse_a = run_verify(d)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(inp.num_blocks)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    inp.k_cache = np.ascontiguousarray(inp.k_cache[perm])
+    inp.v_cache = np.ascontiguousarray(inp.v_cache[perm])
+    tab = inp.block_table.copy()
+    tab[tab >= 0] = inv[tab[tab >= 0]]
+    inp.block_table = tab
+    d2 = to_device(inp)
+    say("verify block permutation B")
+    out_b, lse_b = run_verify(d2)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
+def test_verify_ancestor_only_dependence():
+    # perturb tree node j's key/value: rows of nodes without j on their root path
+    # must be bit-identical, the others must change
+    base = make_config(2)
+    d = to_device(base)
+    say("perturbation base")
+    out0, _ = run_verify(d)
+    o0 = out0.float().cpu().numpy()
+    words = [int(w) for w in oracle.build_masks(base)]
+    for j in (1, 4, 11):
+        pert = make_config(2)
+        pert.k_tree[j] ^= np.uint16(0x0040)
+        pert.v_tree[j] ^= np.uint16(0x0040)
+        dp = to_device(pert)
+        say(f"perturbation node {j}")
+        out1, _ = run_verify(dp)
+        o1 = out1.float().cpu().numpy()
+        for i in range(12):
+            if words[i] >> j & 1:
+                assert not np.array_equal(o0[i], o1[i]), (i, j)
+            else:
+                np.testing.assert_array_equal(o0[i], o1[i])
+
+
+def test_verify_device_errors_flagged():
+    import tree_attention_verify_attn_amd as ta
+    inp = small_inputs(90, dtype="bf16", B=2, Hq=4, Hkv=2, D=128, prefix_lens=(300, 20))
+    d = to_device(inp, max_prefix_len=300)
+    # prefix length beyond the declared bound -> BAD_PREFIX, no out-of-bounds read
+    d.prefix_lens[1] = 301
+    say("device error: prefix beyond bound")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 6
+    d.prefix_lens[1] = int(inp.prefix_lens[1])
+    # block id out of range
+    good = int(inp.block_table[0, 1])
+    d.block_table[0, 1] = inp.num_blocks + 5
+    say("device error: block id out of range")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 6
+    d.block_table[0, 1] = good
+    # bad parent array
+    root1 = int(inp.tree_offsets[1])
+    d.parents[root1] = 5
+    say("device error: bad parent")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 3
+    d.parents[root1] = -1
+    # the same workspace still works for a clean call afterwards
+    say("device error: clean call after errors")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, "after errors")

@@ -1,0 +1,26 @@
+"""MI355X (gfx950) split tree-verify attention.
+
+A draft tree's queries attend to their sequence's committed prefix (paged KV
+cache, no mask) and to the tree tokens on their root path (ancestor-or-self
+mask); the two pieces are merged exactly by log-sum-exp.  All arithmetic runs in
+hand-written HIP kernels behind the C ABI of ``libtreeattn.so``
+(``include/tree_attn.h``); this package only marshals arguments.
+"""
+from .api import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    TreeAttnError,
+    alloc_workspace,
+    build_mask,
+    get_error,
+    make_shape,
+    merge,
+    prefix,
+    split_tokens,
+    status_string,
+    suffix,
+    verify,
+    workspace_init,
+    workspace_size,
+)
+from .build import LIB_PATH, build_library  # noqa: F401

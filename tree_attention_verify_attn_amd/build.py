@@ -1,0 +1,55 @@
+"""Compile libtreeattn.so (HIP, gfx950) in-tree.
+
+The library is one translation unit (csrc/ta_api.hip includes the kernels), built
+with hipcc for gfx950 only.  Packed-fp32 instruction selection is disabled for
+all device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_DIR, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libtreeattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def sources():
+    return [os.path.join(CSRC, "ta_api.hip")]
+
+
+def build_library(out: str = LIB_PATH, verbose: bool = False) -> str:
+    """Build the shared library to ``out`` (atomically replaced) and return its path."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature flag; drop that noise
+    noise = ("packed-fp32-ops", "not a recognized feature for this target")
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

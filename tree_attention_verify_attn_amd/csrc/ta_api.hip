@@ -1,0 +1,440 @@
+// Host side of libtreeattn.so: argument checks, workspace layout, the work-item
+// size heuristic, and kernel launches.  The C entry points are declared and
+// documented in include/tree_attn.h.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <unordered_map>
+
+#include "ta_kernels.hip"
+#include "tree_attn.h"
+
+namespace ta {
+namespace {
+
+struct DeviceInfo {
+  int cus = 0;
+};
+
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static std::unordered_map<int, DeviceInfo> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DeviceInfo{};
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  DeviceInfo d;
+  if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    d.cus = 0;
+  cache[dev] = d;
+  return d;
+}
+
+// Resident workgroups per CU for a kernel and dynamic LDS size (cached).
+int occupancy(const void* kernel, size_t dyn) {
+  static std::mutex mu;
+  static std::unordered_map<unsigned long long, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const unsigned long long key = (reinterpret_cast<unsigned long long>(kernel) << 8) ^
+                                 (dyn << 1) ^ (static_cast<unsigned long long>(dev) << 40);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, dyn) != hipSuccess)
+    occ = 1;
+  if (occ < 1) occ = 1;
+  cache[key] = occ;
+  return occ;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const ta_shape* s) {
+  if (!s) return kErrInvalidArg;
+  if (s->dtype != TA_DTYPE_F32 && s->dtype != TA_DTYPE_BF16) return kErrInvalidArg;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1) return kErrInvalidArg;
+  if (s->num_q_heads % s->num_kv_heads != 0) return kErrInvalidArg;
+  if (s->batch > kMaxBatch) return kErrUnsupported;
+  if (s->head_dim != 64 && s->head_dim != 128) return kErrUnsupported;
+  if (s->block_size != kBlock) return kErrUnsupported;
+  if (s->max_blocks_per_seq < 1) return kErrInvalidArg;
+  if (s->max_tree_nodes < 1) return kErrInvalidArg;
+  if (s->max_tree_nodes > kMaxTree) return kErrUnsupported;
+  if (s->max_prefix_len < 0) return kErrInvalidArg;
+  if (static_cast<long long>(s->max_prefix_len) > static_cast<long long>(kBlock) * s->max_blocks_per_seq)
+    return kErrInvalidArg;
+  if (s->total_tree_nodes < 0) return kErrInvalidArg;
+  if (s->num_blocks < 0 || (s->max_prefix_len > 0 && s->num_blocks < 1)) return kErrInvalidArg;
+  if (s->split_tokens < 0 || s->split_tokens % kBlock != 0) return kErrInvalidArg;
+  if (s->split_tokens > 4096) return kErrUnsupported;
+  if (!(s->softmax_scale <= 0.f || isfinite(s->softmax_scale))) return kErrInvalidArg;
+  return kOk;
+}
+
+int group_of(const ta_shape* s) { return s->num_q_heads / s->num_kv_heads; }
+
+// XCDs of the current device (gfx950: 32 CUs each); 8 when no device is visible.
+int xcd_count() {
+  int cus = device_info().cus;
+  if (cus <= 0) cus = 8 * kCusPerXcd;
+  int n = cus / kCusPerXcd;
+  if (n < 1) n = 1;
+  if (n > kMaxXcd) n = kMaxXcd;
+  return n;
+}
+
+const void* attn_kernel_ptr(const ta_shape* s, bool fused);
+
+// Resident prefix-pass workgroups per XCD (bounds the splits of one group).
+int xcd_capacity(const ta_shape* s, bool fused) {
+  int cus = device_info().cus;
+  if (cus <= 0) return kCusPerXcd;  // no device: assume one workgroup per CU
+  const int per_xcd = cus / xcd_count();
+  const int spx = cdiv(s->batch, xcd_count());
+  const size_t dyn = 16 * size_t(cdiv((2 * ((spx + 2) / 2) + 2 * spx) * int(sizeof(int)), 16));
+  return per_xcd * occupancy(attn_kernel_ptr(s, fused), dyn);
+}
+
+// Prefix tokens per work item.  Every XCD gets the groups (sequence, KV head,
+// row pass) assigned to it; the chunk is sized so that each XCD has about one
+// resident workgroup per work item, within [64, 4096] tokens.  A group never
+// splits into more chunks than one XCD can hold resident at once (its items
+// wait for each other) nor more than kMaxSplits.
+int choose_chunk(const ta_shape* s, bool fused) {
+  const int P = s->max_prefix_len > 0 ? s->max_prefix_len : 1;
+  const int cap = xcd_capacity(s, fused);
+  const int max_splits = cap < kMaxSplits ? cap : kMaxSplits;
+  const int min_chunk = kBlock * cdiv(cdiv(P, max_splits), kBlock);
+  int chunk;
+  if (s->split_tokens > 0) {
+    chunk = s->split_tokens;
+  } else {
+    const int G = group_of(s);
+    const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
+                             cdiv(s->max_tree_nodes * G, kRowsPerPass);
+    const long long per_xcd = (groups + xcd_count() - 1) / xcd_count();
+    const long long tok = (per_xcd * P + cap - 1) / cap;
+    chunk = static_cast<int>(kBlock * ((tok + kBlock - 1) / kBlock));
+  }
+  if (chunk < kBlock) chunk = kBlock;
+  if (chunk > 4096) chunk = 4096;
+  if (chunk < min_chunk) chunk = min_chunk;
+  return chunk;
+}
+
+WsLayout layout_for(const ta_shape* s, int chunk) {
+  WsLayout L{};
+  const int G = group_of(s);
+  const int D = s->head_dim;
+  L.chunk = chunk;
+  L.n_xcd = xcd_count();
+  L.rp_max = cdiv(s->max_tree_nodes * G, kRowsPerPass);
+  int rows = s->max_tree_nodes * G;
+  if (rows > kRowsPerPass) rows = kRowsPerPass;
+  L.rows_slot = 16 * cdiv(rows, 16);
+  L.slot_floats = L.rows_slot * (D + 2);
+  L.num_groups = s->batch * s->num_kv_heads * L.rp_max;
+  L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
+  // large batches: dense per-XCD numbering from a prefix table; small: static
+  L.table_mode = s->batch >= 64 ? 1 : 0;
+  L.lg_per_xcd = cdiv(L.num_groups, L.n_xcd);
+  L.seq_per_xcd = cdiv(s->batch, L.n_xcd);
+  L.items_per_xcd = L.table_mode ? L.seq_per_xcd * s->num_kv_heads * L.rp_max * L.s_max
+                                 : L.lg_per_xcd * L.s_max;
+  L.arrive_off = sizeof(WsHeader);
+  L.partial_off = align256(L.arrive_off + sizeof(unsigned) * size_t(L.num_groups));
+  L.total = L.partial_off +
+            size_t(L.n_xcd) * size_t(L.items_per_xcd) * L.slot_floats * sizeof(float);
+  return L;
+}
+
+Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
+  Params p{};
+  p.batch = s->batch;
+  p.hq = s->num_q_heads;
+  p.hkv = s->num_kv_heads;
+  p.group = group_of(s);
+  p.head_dim = s->head_dim;
+  p.max_blocks = s->max_blocks_per_seq;
+  p.max_tree = s->max_tree_nodes;
+  p.max_prefix = s->max_prefix_len;
+  p.total_nodes = s->total_tree_nodes;
+  p.num_blocks = s->num_blocks;
+  p.chunk = L.chunk;
+  p.rp_max = L.rp_max;
+  p.rows_slot = L.rows_slot;
+  p.slot_floats = L.slot_floats;
+  p.num_groups = L.num_groups;
+  p.n_xcd = L.n_xcd;
+  p.table_mode = L.table_mode;
+  p.s_max = L.s_max;
+  p.lg_per_xcd = L.lg_per_xcd;
+  p.seq_per_xcd = L.seq_per_xcd;
+  p.items_per_xcd = L.items_per_xcd;
+  const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
+  p.scale_log2 = scale * kLog2e;
+  char* w = static_cast<char*>(ws);
+  p.hdr = reinterpret_cast<WsHeader*>(w);
+  if (w) {
+    p.arrive = reinterpret_cast<unsigned*>(w + L.arrive_off);
+    p.partials = reinterpret_cast<float*>(w + L.partial_off);
+  }
+  return p;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T> constexpr int pipeline_depth() { return sizeof(T) == 2 ? 4 : 1; }
+
+template <typename T, int D, bool FUSED>
+const void* attn_ptr() {
+  return reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED, pipeline_depth<T>()>);
+}
+
+const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
+  if (s->dtype == TA_DTYPE_BF16) {
+    if (s->head_dim == 128) return fused ? attn_ptr<uint16_t, 128, true>() : attn_ptr<uint16_t, 128, false>();
+    return fused ? attn_ptr<uint16_t, 64, true>() : attn_ptr<uint16_t, 64, false>();
+  }
+  if (s->head_dim == 128) return fused ? attn_ptr<float, 128, true>() : attn_ptr<float, 128, false>();
+  return fused ? attn_ptr<float, 64, true>() : attn_ptr<float, 64, false>();
+}
+
+template <typename T, int D, bool FUSED>
+int launch_attn(Params p, const WsLayout& L, hipStream_t stream) {
+  constexpr int PD = pipeline_depth<T>();
+  const void* kern = attn_ptr<T, D, FUSED>();
+  const size_t dyn = p.table_mode ? 16 * size_t(cdiv((2 * ((p.seq_per_xcd + 2) / 2) + 2 * p.seq_per_xcd) * int(sizeof(int)), 16)) : 0;
+  const int cus = device_info().cus;
+  if (cus <= 0) return kErrHip;
+  const int cap = (cus / L.n_xcd) * occupancy(kern, dyn);
+  int first = L.items_per_xcd < cap ? L.items_per_xcd : cap;
+  if (first < 1) first = 1;
+  p.first_round = first;
+  hipLaunchKernelGGL((attn_kernel<T, D, FUSED, PD>), dim3(unsigned(first * L.n_xcd)),
+                     dim3(kThreads), dyn, stream, p);
+  return launch_status();
+}
+
+template <bool FUSED>
+int dispatch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
+  if (s->dtype == TA_DTYPE_BF16) {
+    if (s->head_dim == 128) return launch_attn<uint16_t, 128, FUSED>(p, L, stream);
+    return launch_attn<uint16_t, 64, FUSED>(p, L, stream);
+  }
+  if (s->head_dim == 128) return launch_attn<float, 128, FUSED>(p, L, stream);
+  return launch_attn<float, 64, FUSED>(p, L, stream);
+}
+
+int check_ws(const ta_shape* s, const WsLayout& L, void* ws, size_t ws_bytes) {
+  (void)s;
+  if (!ws || !aligned16(ws)) return kErrWorkspace;
+  if (ws_bytes < L.total) return kErrWorkspace;
+  return kOk;
+}
+
+}  // namespace
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" {
+
+size_t tree_attn_workspace_size(const ta_shape* shape) {
+  if (check_shape(shape) != kOk) return 0;
+  const size_t a = layout_for(shape, choose_chunk(shape, true)).total;
+  const size_t b = layout_for(shape, choose_chunk(shape, false)).total;
+  return a > b ? a : b;
+}
+
+int32_t tree_attn_split_tokens(const ta_shape* shape) {
+  if (check_shape(shape) != kOk) return 0;
+  return choose_chunk(shape, true);
+}
+
+ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned16(ws)) return TA_ERR_INVALID_ARG;
+  if (ws_bytes == 0) return TA_OK;
+  const size_t n16 = ws_bytes / 16;
+  const size_t tail = ws_bytes % 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(ws_init_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<uint4*>(ws), n16, static_cast<char*>(ws) + n16 * 16, tail);
+  return static_cast<ta_status>(launch_status());
+}
+
+ta_status tree_attn_build_mask(const ta_shape* shape, const int32_t* parents,
+                               const int32_t* tree_offsets, uint64_t* mask_out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!tree_offsets || !mask_out || (shape->total_tree_nodes > 0 && !parents))
+    return TA_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < sizeof(WsHeader)) return TA_ERR_WORKSPACE;
+  WsLayout L = layout_for(shape, kBlock);
+  Params p = base_params(shape, L, ws);
+  p.parents = parents;
+  p.tree_offsets = tree_offsets;
+  hipLaunchKernelGGL(mask_kernel, dim3(unsigned(shape->batch)), dim3(64), 0, stream, p, mask_out);
+  return static_cast<ta_status>(launch_status());
+}
+
+ta_status tree_attn_prefix(const ta_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* prefix_lens, const int32_t* tree_offsets,
+                           float* o_prefix, float* lse_prefix, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!prefix_lens || !tree_offsets || !lse_prefix || !block_table) return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!q || !o_prefix)) return TA_ERR_INVALID_ARG;
+  if (shape->max_prefix_len > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_prefix))
+    return TA_ERR_INVALID_ARG;
+  WsLayout L = layout_for(shape, choose_chunk(shape, false));
+  st = check_ws(shape, L, ws, ws_bytes);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->total_tree_nodes == 0) return TA_OK;
+  Params p = base_params(shape, L, ws);
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.prefix_lens = prefix_lens;
+  p.tree_offsets = tree_offsets;
+  p.out = o_prefix;
+  p.lse_out = lse_prefix;
+  return static_cast<ta_status>(dispatch_attn<false>(shape, p, L, stream));
+}
+
+ta_status tree_attn_suffix(const ta_shape* shape, const void* q, const void* k_tree,
+                           const void* v_tree, const uint64_t* mask,
+                           const int32_t* tree_offsets, float* o_suffix, float* lse_suffix,
+                           hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!tree_offsets || !lse_suffix) return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !mask || !o_suffix))
+    return TA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(o_suffix))
+    return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes == 0) return TA_OK;
+  WsLayout L = layout_for(shape, kBlock);
+  Params p = base_params(shape, L, nullptr);
+  p.q = q;
+  p.k_tree = k_tree;
+  p.v_tree = v_tree;
+  p.mask_in = mask;
+  p.tree_offsets = tree_offsets;
+  p.out = o_suffix;
+  p.lse_out = lse_suffix;
+  const unsigned grid = unsigned(L.num_groups);
+  if (shape->dtype == TA_DTYPE_BF16) {
+    if (shape->head_dim == 128)
+      hipLaunchKernelGGL((suffix_kernel<uint16_t, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((suffix_kernel<uint16_t, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    if (shape->head_dim == 128)
+      hipLaunchKernelGGL((suffix_kernel<float, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((suffix_kernel<float, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
+  }
+  return static_cast<ta_status>(launch_status());
+}
+
+ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype, const float* o_a,
+                          const float* lse_a, const float* o_b, const float* lse_b, void* out,
+                          float* lse_out, hipStream_t stream) {
+  if (rows < 0 || head_dim < 4 || head_dim % 4 != 0) return TA_ERR_INVALID_ARG;
+  if (out_dtype != TA_DTYPE_F32 && out_dtype != TA_DTYPE_BF16) return TA_ERR_INVALID_ARG;
+  if (rows == 0) return TA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !out) return TA_ERR_INVALID_ARG;
+  if (!aligned16(o_a) || !aligned16(o_b)) return TA_ERR_INVALID_ARG;
+  const long long n = rows * (head_dim / 4);
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (out_dtype == TA_DTYPE_BF16)
+    hipLaunchKernelGGL((merge_kernel<uint16_t>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<long long>(rows), int(head_dim), o_a, lse_a, o_b, lse_b,
+                       static_cast<uint16_t*>(out), lse_out);
+  else
+    hipLaunchKernelGGL((merge_kernel<float>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<long long>(rows), int(head_dim), o_a, lse_a, o_b, lse_b,
+                       static_cast<float*>(out), lse_out);
+  return static_cast<ta_status>(launch_status());
+}
+
+ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* prefix_lens, const void* k_tree, const void* v_tree,
+                           const int32_t* parents, const int32_t* tree_offsets, void* out,
+                           float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!prefix_lens || !tree_offsets || !block_table) return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !parents || !out))
+    return TA_ERR_INVALID_ARG;
+  if (shape->max_prefix_len > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
+      !aligned16(v_tree))
+    return TA_ERR_INVALID_ARG;
+  WsLayout L = layout_for(shape, choose_chunk(shape, true));
+  st = check_ws(shape, L, ws, ws_bytes);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->total_tree_nodes == 0) return TA_OK;
+  Params p = base_params(shape, L, ws);
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.prefix_lens = prefix_lens;
+  p.k_tree = k_tree;
+  p.v_tree = v_tree;
+  p.parents = parents;
+  p.tree_offsets = tree_offsets;
+  p.out = out;
+  p.lse_out = lse_out;
+  return static_cast<ta_status>(dispatch_attn<true>(shape, p, L, stream));
+}
+
+ta_status tree_attn_get_error(void* ws, hipStream_t stream) {
+  if (!ws) return TA_ERR_INVALID_ARG;
+  int err = 0;
+  if (hipMemcpyAsync(&err, ws, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return TA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return TA_ERR_HIP;
+  if (err != 0) {
+    const int zero = 0;
+    if (hipMemcpyAsync(ws, &zero, sizeof(int), hipMemcpyHostToDevice, stream) != hipSuccess)
+      return TA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return TA_ERR_HIP;
+  }
+  return static_cast<ta_status>(err);
+}
+
+const char* tree_attn_status_string(ta_status status) {
+  switch (status) {
+    case TA_OK: return "ok";
+    case TA_ERR_INVALID_ARG: return "invalid argument (scalar, null or misaligned pointer)";
+    case TA_ERR_UNSUPPORTED: return "unsupported shape";
+    case TA_ERR_BAD_TREE: return "invalid tree: parent array or tree_offsets (device check)";
+    case TA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case TA_ERR_BAD_PREFIX: return "prefix length or KV block id out of range (device check)";
+    case TA_ERR_TIMEOUT: return "a bounded cross-workgroup wait gave up (device check)";
+    case TA_ERR_PLACEMENT: return "a workgroup ran on an unexpected XCD (device check)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

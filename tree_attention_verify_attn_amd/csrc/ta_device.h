@@ -1,0 +1,121 @@
+// Device helpers for the gfx950 tree-verify attention kernels: element types,
+// bf16 conversion, wave reductions, MFMA wrappers, and the tree-mask builder.
+#pragma once
+
+#include "ta_common.h"
+
+namespace ta {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- elements
+// bf16 tensors are handled as their raw 16-bit patterns (uint16_t).
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(u) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  // hardware conversion, round to nearest even
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load_f(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ uint16_t from_f(float f) { return f32_to_bf16(f); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load_f(const float* p) { return *p; }
+  static __device__ __forceinline__ float from_f(float f) { return f; }
+};
+
+// Dot product of 16 bytes of q with 16 bytes of k, accumulated in fp32.
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, uint16_t) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(bf16_to_f32(static_cast<uint16_t>(av[i])), bf16_to_f32(static_cast<uint16_t>(bv[i])), acc);
+    acc = fmaf(bf16_to_f32(static_cast<uint16_t>(av[i] >> 16)), bf16_to_f32(static_cast<uint16_t>(bv[i] >> 16)), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, float) {
+  acc = fmaf(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, b.x), acc);
+  acc = fmaf(__builtin_bit_cast(float, a.y), __builtin_bit_cast(float, b.y), acc);
+  acc = fmaf(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, b.z), acc);
+  acc = fmaf(__builtin_bit_cast(float, a.w), __builtin_bit_cast(float, b.w), acc);
+  return acc;
+}
+
+// -------------------------------------------------------------- math
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA output row).
+__device__ __forceinline__ float max_over_quads(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_quads(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+// Reductions over a 32-lane half-wave.
+__device__ __forceinline__ float max_over_32(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_32(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 32);
+  return v;
+}
+
+__device__ __forceinline__ void set_error(WsHeader* h, int code) {
+  if (h) atomicCAS(&h->error, 0, code);
+}
+
+// ------------------------------------------------------------ tree mask
+// One wave builds the ancestor-or-self words of one tree of T <= 64 nodes by
+// pointer jumping: every lane i keeps the set of its ancestors within distance
+// < 2^k and a link to its 2^k-th ancestor; one round ORs in the set held by that
+// ancestor and follows its link, doubling the distance.  Six rounds reach any
+// depth below 64.  Lanes >= T return 0.  `bad` is set (wave-uniformly) when a
+// parent is neither -1 nor an earlier node; such a parent is treated as -1.
+// [tree mask of the draft-token piece: pith.science review of arXiv
+// 2508.08192, "What carries the argument"; ancestor-or-self as in SpecInfer]
+__device__ __forceinline__ uint64_t tree_mask_wave(const int32_t* parents, int T, bool& bad) {
+  const int lane = threadIdx.x & 63;
+  int up = -1;
+  bool lane_bad = false;
+  if (lane < T) {
+    int p = parents[lane];
+    lane_bad = !(p == -1 || (p >= 0 && p < lane));
+    up = lane_bad ? -1 : p;
+  }
+  uint64_t anc = lane < T ? (uint64_t(1) << lane) : 0;
+#pragma unroll
+  for (int round = 0; round < 6; ++round) {
+    const int src = up >= 0 ? up : lane;
+    const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src);
+    const uint32_t hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+    const int up2 = __shfl(up, src);
+    if (up >= 0) {
+      anc |= (static_cast<uint64_t>(hi) << 32) | lo;
+      up = up2;
+    }
+  }
+  bad = __any(lane_bad);
+  return anc;
+}
+
+__device__ __forceinline__ uint64_t low_bits(int T) {
+  return T >= 64 ? ~uint64_t(0) : ((uint64_t(1) << T) - 1);
+}
+
+}  // namespace ta

@@ -1,0 +1,925 @@
+// gfx950 kernels of the split tree-verify attention library.
+//
+// Method: each draft-tree query attends to (a) its sequence's committed prefix,
+// read through a paged KV cache, with no mask, and (b) the tree tokens on its
+// root path.  The two partial results are combined exactly through their
+// log-sum-exp.  [pith.science review of arXiv 2508.08192, "What carries the
+// argument"; merge over disjoint KV chunks: Hydragen, Juravsky et al. 2024,
+// pith.science verdict record, pith_extraction.supporting_citations; paged KV:
+// PagedAttention, Kwon et al. 2023, same field]
+//
+// Kernels
+//   ws_init_kernel   zero-fill of a workspace (graph-capture safe)
+//   mask_kernel      ancestor-or-self mask words of every tree (one wave per tree)
+//   attn_kernel      prefix pass; with FUSED it also builds the tree mask, runs
+//                    the tree piece and merges (the fused verify)
+//   suffix_kernel    tree piece on its own (split path)
+//   merge_kernel     merge of two (o, lse) results (split path)
+//
+// attn_kernel, one work item = sequence b, KV head g, row pass rp, prefix chunk s:
+//   * the grouped query rows of (b, g) -- tree node i times the G query heads
+//     sharing KV head g -- form up to four 16-row MFMA tiles, one per wave;
+//   * the chunk's 64-token KV blocks stream HBM -> registers -> LDS (K row-major
+//     with an XOR chunk swizzle, V transposed), PD blocks in flight;
+//   * per block each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a
+//     lane holds one query row and the online softmax needs only the cross-lane
+//     steps l^16, l^32; P^T then feeds O^T += V^T P^T as the MFMA B operand
+//     straight from registers;
+//   * the chunk's partial (unnormalised o, running max, running sum) goes to the
+//     workspace; the items of one group -- all on one XCD, so the exchange stays
+//     in that XCD's L2 -- meet at a counter and split the final combine: each
+//     takes some rows, folds every chunk partial and (fused) the row's tree piece
+//     with their log-sum-exp weights, and writes the output row.
+#include <type_traits>
+
+#include "ta_device.h"
+
+namespace ta {
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ unsigned ld_counter(const unsigned* p) {
+  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// XCD this wave runs on (hardware register XCC_ID, bits [3:0]).
+__device__ __forceinline__ int xcc_id() {
+  return int(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)));
+}
+
+// =============================================================== utilities
+__global__ void __launch_bounds__(256) ws_init_kernel(uint4* ws, size_t n16, char* tail,
+                                                     size_t ntail) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    ws[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// Per-sequence facts, validated.  Invalid data is replaced by an empty tree or
+// an empty prefix so that no later read goes out of bounds.
+struct SeqInfo {
+  int off, T, P, S, RP, items;
+};
+
+__device__ __forceinline__ SeqInfo make_seq(const Params& p, int o0, int o1, int P, bool flag) {
+  SeqInfo s;
+  int T = o1 - o0;
+  const bool tree_ok = o0 >= 0 && o1 >= o0 && o1 <= p.total_nodes && T <= p.max_tree;
+  const bool p_ok = P >= 0 && P <= p.max_prefix;
+  if (!tree_ok) {
+    if (flag) set_error(p.hdr, kErrBadTree);
+    T = 0;
+    o0 = 0;
+  }
+  if (!p_ok) {
+    if (flag) set_error(p.hdr, kErrBadPrefix);
+    P = 0;
+  }
+  s.off = o0;
+  s.T = T;
+  s.P = P;
+  s.S = P > 0 ? cdiv(P, p.chunk) : 1;
+  s.RP = cdiv(T * p.group, kRowsPerPass);
+  s.items = p.hkv * s.RP * s.S;
+  return s;
+}
+
+__device__ __forceinline__ SeqInfo seq_info(const Params& p, int b, bool flag) {
+  return make_seq(p, p.tree_offsets[b], p.tree_offsets[b + 1], p.prefix_lens[b], flag);
+}
+
+// Table numbering: cum[j] = items of this XCD's sequences before local sequence
+// j (sequence b = j * n_xcd + x); srp[j] = (chunks, row passes) of sequence j.
+// Returns this XCD's item count.
+__device__ int build_xcd_table(const Params& p, int x, int* cum, int2* srp, int* scratch) {
+  const int tid = threadIdx.x;
+  const int n = p.seq_per_xcd;
+  const int per = cdiv(n, kThreads);
+  const int j0 = min(n, tid * per);
+  const int j1 = min(n, j0 + per);
+  const bool flag = blockIdx.x < unsigned(p.n_xcd);
+  int local = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int b = j * p.n_xcd + x;
+    SeqInfo si = b < p.batch ? seq_info(p, b, flag) : SeqInfo{0, 0, 0, 1, 0, 0};
+    cum[j + 1] = si.items;
+    srp[j] = make_int2(si.S, si.RP);
+    local += si.items;
+  }
+  scratch[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int v = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? scratch[tid - 1] : 0;
+  for (int j = j0; j < j1; ++j) {
+    run += cum[j + 1];
+    cum[j + 1] = run;
+  }
+  if (tid == 0) {
+    cum[0] = 0;
+    if (blockIdx.x == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
+      set_error(p.hdr, kErrBadTree);
+  }
+  __syncthreads();
+  return cum[n];
+}
+
+struct Item {
+  int b, g, rp, s, grp;
+  bool valid;  // false: the static numbering names a group that does not exist
+};
+
+// Decode item li of XCD x into (sequence, KV head, row pass, chunk) without any
+// global-memory read, so that the item's first loads can all be issued at once.
+// Static numbering may name a chunk or row pass the sequence does not have; the
+// item is then found empty once the sequence's facts arrive.
+__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int2* srp,
+                                            int x, int li) {
+  Item it;
+  it.valid = true;
+  if (p.table_mode == 0) {
+    const int lg = li / p.s_max;
+    it.s = li % p.s_max;
+    const int k = lg * p.n_xcd + x;
+    it.valid = k < p.num_groups;
+    it.grp = it.valid ? k : 0;
+    it.rp = it.grp % p.rp_max;
+    const int bg = it.grp / p.rp_max;
+    it.g = bg % p.hkv;
+    it.b = bg / p.hkv;
+    return it;
+  }
+  int lo = 0, hi = p.seq_per_xcd;  // largest j with cum[j] <= li
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] <= li) lo = mid; else hi = mid;
+  }
+  it.b = lo * p.n_xcd + x;
+  const int S = srp[lo].x, RP = srp[lo].y;
+  const int local = li - cum[lo];
+  it.s = local % S;
+  const int t = local / S;
+  it.rp = t % RP;
+  it.g = t / RP;
+  it.grp = (it.b * p.hkv + it.g) * p.rp_max + it.rp;
+  return it;
+}
+
+// ====================================================== suffix (tree) piece
+// D/4 consecutive lanes (one "row slot") compute the tree piece of one grouped
+// query row: the keys are the tree nodes whose bit is set in `word`.  Lane d4
+// of the slot scores keys d4, d4 + D/4, ... and owns output elements
+// [4*d4, 4*d4 + 4).  Returns the max m (log2 units: scores carry
+// softmax_scale*log2 e), l = sum of 2^(s - m) and the lane's four unnormalised
+// outputs.  No visible key gives m = -inf, l = 0, o = 0.
+// [draft-token piece that needs the tree mask: pith.science review,
+// "What carries the argument"]
+template <typename T, int D>
+struct TreeSrc {
+  const T* q;        // this row's query, D elements
+  const T* k;        // row j of tree K at k + j * k_stride (chunks XOR-swizzled if swz)
+  const T* v;        // row j of tree V at v + j * v_stride
+  int k_stride, v_stride;
+  bool swz;
+};
+
+template <typename T, int D>
+__device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word,
+                         float scale_log2, float& m_out, float& l_out, float4& o_out) {
+  constexpr int L4 = D / 4;
+  constexpr int KPL = kMaxTree / L4;  // keys scored per lane
+  constexpr int KCH = D * int(sizeof(T)) / 16;
+  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
+  word &= low_bits(Tn);
+  const uint4* q16 = reinterpret_cast<const uint4*>(src.q);
+  float s[KPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const int jj = d4 + L4 * k;
+    const bool vis = (word >> jj) & 1;
+    float dot = 0.f;
+    if (vis) {
+      const uint4* krow = reinterpret_cast<const uint4*>(src.k + size_t(jj) * src.k_stride);
+#pragma unroll 4
+      for (int c = 0; c < KCH; ++c) {
+        const int pc = src.swz ? (c ^ (jj & SWZ)) : c;
+        dot = dot16(q16[c], krow[pc], dot, T());
+      }
+    }
+    s[k] = vis ? dot * scale_log2 : -INFINITY;
+    m = fmaxf(m, s[k]);
+  }
+#pragma unroll
+  for (int x = 1; x < L4; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, L4));
+  o_out = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (m == -INFINITY) {
+    m_out = -INFINITY;
+    l_out = 0.f;
+    return;
+  }
+  float pk[KPL];
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    pk[k] = s[k] == -INFINITY ? 0.f : exp2_fast(s[k] - m);
+    l += pk[k];
+  }
+#pragma unroll
+  for (int x = 1; x < L4; x <<= 1) l += __shfl_xor(l, x, L4);
+  uint64_t bits = word;
+  while (bits) {
+    const int jj = __builtin_ctzll(bits);
+    bits &= bits - 1;
+    float mine = pk[0];
+#pragma unroll
+    for (int k = 1; k < KPL; ++k) mine = (jj / L4 == k) ? pk[k] : mine;
+    const float pj = __shfl(mine, jj % L4, L4);
+    const T* vrow = src.v + size_t(jj) * src.v_stride + 4 * d4;
+    float v[4];
+    if constexpr (sizeof(T) == 2) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(vrow);
+      v[0] = bf16_to_f32(uint16_t(raw.x)); v[1] = bf16_to_f32(uint16_t(raw.x >> 16));
+      v[2] = bf16_to_f32(uint16_t(raw.y)); v[3] = bf16_to_f32(uint16_t(raw.y >> 16));
+    } else {
+      const float4 raw = *reinterpret_cast<const float4*>(vrow);
+      v[0] = raw.x; v[1] = raw.y; v[2] = raw.z; v[3] = raw.w;
+    }
+    o_out.x = fmaf(pj, v[0], o_out.x);
+    o_out.y = fmaf(pj, v[1], o_out.y);
+    o_out.z = fmaf(pj, v[2], o_out.z);
+    o_out.w = fmaf(pj, v[3], o_out.w);
+  }
+  m_out = m;
+  l_out = l;
+}
+
+// =========================================================== prefix piece
+template <typename T, int D>
+struct Smem {
+  static constexpr int KCH = D * int(sizeof(T)) / 16;  // 16-byte chunks per K row
+  static constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
+  static constexpr int VP = kBlock + 4;                // V^T row pitch (elements)
+  alignas(16) unsigned char k[kBlock * KCH * 16];      // K block / combine scratch
+  alignas(16) T vt[D * VP];                            // V block transposed
+  alignas(16) T tk[kMaxTree * D];                      // tree K rows (swizzled chunks)
+  alignas(16) T tv[kMaxTree * D];                      // tree V rows
+  uint64_t mask[kMaxTree];
+  int scratch[kThreads];
+  int bcast[4];
+};
+
+template <typename T> struct VLoad;                // per-lane bytes of one V row
+template <> struct VLoad<uint16_t> { using d64 = uint16_t; using d128 = uint32_t; };
+template <> struct VLoad<float> { using d64 = float; using d128 = uint2; };
+
+template <typename T, int D> struct Traits {
+  static constexpr int KCH = D * int(sizeof(T)) / 16;
+  static constexpr int KPT = kBlock * KCH / kThreads;     // K chunks per thread per block
+  static constexpr int TPT = kMaxTree * KCH / kThreads;   // tree-row chunks per thread
+  static constexpr int DPL = D / 64;                      // head-dim elements per lane in V rows
+  using VT = typename std::conditional<D == 64, typename VLoad<T>::d64,
+                                       typename VLoad<T>::d128>::type;
+  static constexpr int QCH = D / 4 * int(sizeof(T)) / 16; // 16-byte chunks of the Q fragment
+  static constexpr int DT = D / 16;                       // 16-wide head-dim tiles of O^T
+};
+
+// element e (0..DPL-1) of one staged V word, as raw bits
+template <typename T, int D>
+__device__ __forceinline__ uint32_t v_elem(typename Traits<T, D>::VT w, int e) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (D == 64) return w;
+    else return e == 0 ? (w & 0xffffu) : (w >> 16);
+  } else {
+    if constexpr (D == 64) return __builtin_bit_cast(uint32_t, w);
+    else return e == 0 ? w.x : w.y;
+  }
+}
+
+template <typename T, int D, bool FUSED, int PD>
+__device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, int slot_index) {
+  const int lane0 = threadIdx.x & 63;
+  // block ids of the chunk (lane j: block j) and the sequence's facts, read in
+  // one round trip; ids past the sequence's prefix are never used
+  int my_id = -1;
+  {
+    const int lb = it.s * (p.chunk / kBlock) + lane0;
+    if (lane0 < p.chunk / kBlock && lb < p.max_blocks)
+      my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
+  }
+  const SeqInfo si = seq_info(p, it.b, false);
+  if (it.rp >= si.RP || it.s >= si.S) return;  // static numbering: no such item
+  using Tr = Traits<T, D>;
+  using VT = typename Tr::VT;
+  constexpr int KCH = Tr::KCH, KPT = Tr::KPT, TPT = Tr::TPT, DPL = Tr::DPL, QCH = Tr::QCH,
+                DT = Tr::DT;
+  constexpr int VP = Smem<T, D>::VP, SWZ = Smem<T, D>::SWZ;
+  constexpr bool kBf16 = sizeof(T) == 2;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int lr = lane & 15;
+  const int kq = lane >> 4;
+
+  const int G = p.group;
+  const int R = si.T * G;
+  const int rlo = it.rp * kRowsPerPass;
+  const int rcount = min(kRowsPerPass, R - rlo);
+  const int RT = cdiv(rcount, 16);
+  const int t0 = it.s * p.chunk;
+  const int ntok = max(0, min(si.P, t0 + p.chunk) - t0);
+  const int nblk = cdiv(ntok, kBlock);
+  const int S = si.S;
+
+
+  uint4 kreg[PD][KPT];
+  VT vreg[PD][16];
+  int nv[PD];
+  const size_t head_stride = size_t(kBlock) * D;  // elements per (block, head)
+  auto issue = [&](int st, int j) {
+    int id = __shfl(my_id, j);
+    const bool ok = id >= 0 && id < p.num_blocks;
+    if (!ok) {
+      if (tid == 0) set_error(p.hdr, kErrBadPrefix);
+      id = 0;
+    }
+    nv[st] = ok ? min(kBlock, ntok - j * kBlock) : 0;
+    const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      kreg[st][i] = *reinterpret_cast<const uint4*>(kb + size_t(i * kThreads + tid) * 16);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      vreg[st][k] = *reinterpret_cast<const VT*>(vb + (size_t(16 * w + k) * D + lane * DPL) * sizeof(T));
+  };
+  auto store = [&](int st) {
+    const int nvalid = nv[st];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = i * kThreads + tid;
+      const int tok = u / KCH;
+      const int c = u % KCH;
+      const uint4 val = tok < nvalid ? kreg[st][i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sm.k + (tok * KCH + (c ^ (tok & SWZ))) * 16) = val;
+    }
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        uint32_t xv[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int tok = 16 * w + 4 * gi + tt;
+          xv[tt] = tok < nvalid ? v_elem<T, D>(vreg[st][4 * gi + tt], e) : 0u;
+        }
+        T* dst = sm.vt + (lane * DPL + e) * VP + 16 * w + 4 * gi;
+        if constexpr (kBf16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(xv[0] | (xv[1] << 16), xv[2] | (xv[3] << 16));
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+        }
+      }
+    }
+  };
+
+  // ---- issue the first PD blocks
+#pragma unroll
+  for (int st = 0; st < PD; ++st)
+    if (st < nblk) issue(st, st);
+
+  // ---- tree rows and parents of (b, g) (fused): loaded now, staged into LDS
+  // with the first block.  Addresses are clamped to row T-1 so every load is
+  // unconditional and in bounds.
+  uint4 tkr[FUSED ? TPT : 1], tvr[FUSED ? TPT : 1];
+  int par = -1;
+  if constexpr (FUSED) {
+    const int Tn = si.T;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int u = i * kThreads + tid;
+      const int row = min(u / KCH, Tn - 1);
+      const int c = u % KCH;
+      const size_t roff = (size_t(si.off + row) * p.hkv + it.g) * D;
+      tkr[i] = reinterpret_cast<const uint4*>(static_cast<const T*>(p.k_tree) + roff)[c];
+      tvr[i] = reinterpret_cast<const uint4*>(static_cast<const T*>(p.v_tree) + roff)[c];
+    }
+    if (w == 0) par = p.parents[si.off + min(lane, Tn - 1)];
+  }
+
+  // ---- Q fragment of this wave's row tile: lane (row lr, group kq) holds the
+  // contiguous head-dim range [kq*D/4, (kq+1)*D/4) of its row.
+  const bool active = w < RT;
+  uint4 qv[QCH];
+  {
+    const int r = 16 * w + lr;
+    if (active && r < rcount) {
+      const int rr = rlo + r;
+      const int h = it.g * G + rr % G;
+      const uint4* src = reinterpret_cast<const uint4*>(
+          static_cast<const T*>(p.q) + (size_t(si.off + rr / G) * p.hq + h) * D + kq * (D / 4));
+#pragma unroll
+      for (int c = 0; c < QCH; ++c) qv[c] = src[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < QCH; ++c) qv[c] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  auto stage_tree = [&]() {
+    if constexpr (FUSED) {
+      const int Tn = si.T;
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int u = i * kThreads + tid;
+        const int row = u / KCH;
+        const int c = u % KCH;
+        if (row < Tn) {
+          reinterpret_cast<uint4*>(sm.tk + row * D)[c ^ (row & SWZ)] = tkr[i];
+          reinterpret_cast<uint4*>(sm.tv + row * D)[c] = tvr[i];
+        }
+      }
+      if (w == 0) {
+        // ancestor-or-self words by pointer jumping (as in tree_mask_wave)
+        const bool bad_lane = lane < Tn && !(par == -1 || (par >= 0 && par < lane));
+        int up = (lane < Tn && !bad_lane) ? par : -1;
+        uint64_t anc = lane < Tn ? (uint64_t(1) << lane) : 0;
+#pragma unroll
+        for (int round = 0; round < 6; ++round) {
+          const int src = up >= 0 ? up : lane;
+          const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src);
+          const uint32_t hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+          const int up2 = __shfl(up, src);
+          if (up >= 0) {
+            anc |= (static_cast<uint64_t>(hi) << 32) | lo;
+            up = up2;
+          }
+        }
+        sm.mask[lane] = anc;
+        if (__any(bad_lane) && lane == 0 && it.s == 0 && it.g == 0 && it.rp == 0)
+          set_error(p.hdr, kErrBadTree);
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int nvalid) {
+    // every LDS read of the block is issued before the MFMAs that consume it,
+    // so the reads overlap instead of each waiting its own round trip
+    uint4 kf[4][QCH];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + lr;
+      const unsigned char* krow = sm.k + tok * KCH * 16;
+#pragma unroll
+      for (int c = 0; c < QCH; ++c) {
+        const int lc = kq * QCH + c;  // logical 16-byte chunk of the K row
+        kf[tt][c] = *reinterpret_cast<const uint4*>(krow + ((lc ^ (tok & SWZ)) * 16));
+      }
+    }
+    floatx4 sacc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < QCH; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if constexpr (kBf16) {
+          sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kf[tt][c]), __builtin_bit_cast(bf16x8, qv[c]), sacc[tt],
+              0, 0, 0);
+        } else {
+          const uint4 kv = kf[tt][c];
+          const float ka[4] = {__builtin_bit_cast(float, kv.x), __builtin_bit_cast(float, kv.y),
+                               __builtin_bit_cast(float, kv.z), __builtin_bit_cast(float, kv.w)};
+          const float qa[4] = {__builtin_bit_cast(float, qv[c].x), __builtin_bit_cast(float, qv[c].y),
+                               __builtin_bit_cast(float, qv[c].z), __builtin_bit_cast(float, qv[c].w)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[tt], 0, 0, 0);
+        }
+      }
+    // V^T fragments for the PV product, read while the softmax runs
+    constexpr int NVF = kBf16 ? 2 * DT : 4 * DT;
+    uint4 vf[NVF];
+#pragma unroll
+    for (int f = 0; f < NVF; ++f) {
+      if constexpr (kBf16) {
+        const int kk = f / DT, dt = f % DT;
+        const T* vrow = sm.vt + (16 * dt + lr) * VP + 32 * kk + 4 * kq;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        vf[f] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        const int tt = f / DT, dt = f % DT;
+        vf[f] = *reinterpret_cast<const uint4*>(sm.vt + (16 * dt + lr) * VP + 16 * tt + 4 * kq);
+      }
+    }
+    // lane (row lr, group kq) holds tokens 16*tt + 4*kq + i of its row
+    float sc[4][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * kq + i;
+        sc[tt][i] = tok < nvalid ? sacc[tt][i] * p.scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, sc[tt][i]);
+      }
+    bmax = max_over_quads(bmax);
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    // rescale the running output only when some row's max rose (alpha == 1 else)
+    if (__any(m_new > m_run)) {
+      const float alpha = exp2_fast(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    m_run = m_new;
+    float pr[4][4];
+    float rsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e = exp2_fast(sc[tt][i] - m_use);
+        if constexpr (kBf16) e = bf16_to_f32(f32_to_bf16(e));  // the value the MFMA sees
+        pr[tt][i] = e;
+        rsum += e;
+      }
+    rsum = sum_over_quads(rsum);
+    l_run += rsum;
+
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 bp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bp[i] = static_cast<__bf16>(pr[2 * kk][i]);
+          bp[4 + i] = static_cast<__bf16>(pr[2 * kk + 1][i]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, vf[kk * DT + dt]), bp, oacc[dt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint4 a = vf[tt * DT + dt];
+          const float av[4] = {__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y),
+                               __builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], pr[tt][i], oacc[dt], 0, 0, 0);
+        }
+    }
+  };
+
+  // ---- stream the chunk: PD blocks in flight, one block resident in LDS
+  if (nblk == 0) stage_tree();
+  for (int jb = 0; jb < nblk; jb += PD) {
+#pragma unroll
+    for (int st = 0; st < PD; ++st) {
+      const int j = jb + st;
+      if (j < nblk) {
+        __syncthreads();  // everyone is done reading the previous block
+        store(st);
+        if (j == 0) stage_tree();
+        const int nvalid = nv[st];
+        if (j + PD < nblk) issue(st, j + PD);
+        __syncthreads();
+        if (active) compute(nvalid);
+      }
+    }
+  }
+
+  // ---- chunk partial -> workspace (plain stores: read back in this XCD's L2)
+  float* slot = p.partials + size_t(slot_index) * p.slot_floats;
+  if (active) {
+    const int r = 16 * w + lr;
+    if (r < rcount) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<floatx4*>(slot + r * D + 16 * dt + 4 * kq) = oacc[dt];
+      if (kq == 0) {
+        slot[p.rows_slot * D + r] = m_run;
+        slot[p.rows_slot * D + p.rows_slot + r] = l_run;
+      }
+    }
+  }
+
+  // ---- meet the other chunks of the group (all on this XCD)
+  wait_all_mem();  // this wave's partial stores have reached L2
+  __syncthreads();
+  if (S > 1) {
+    if (tid == 0) {
+      atomicAdd(p.arrive + it.grp, 1u);
+      unsigned spins = 0;
+      int timed_out = 0;
+      while (ld_counter(p.arrive + it.grp) < unsigned(S)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          timed_out = 1;
+          break;
+        }
+      }
+      if (timed_out) set_error(p.hdr, kErrTimeout);
+      sm.bcast[2] = timed_out;
+    }
+    __syncthreads();
+    if (sm.bcast[2]) return;
+  }
+
+  // ---- combine.  The S items of the group share its rows: item s takes rows
+  // s, s + S, ...  For one row, D/4 lanes (a row slot) cover the head dim, 4
+  // elements each; QG row slots split the S chunk partials between them (all
+  // loads issued up front), then meet in LDS.  Chunk partials and, in the fused
+  // kernel, the row's tree piece are folded with their log-sum-exp weights.
+  // [merge_attentions over disjoint KV chunks: pith.science verdict record,
+  // pith_extraction.supporting_citations (Juravsky et al. 2024)]
+  {
+    constexpr int L4 = D / 4;
+    constexpr int NSLOT = kThreads / L4;
+    constexpr int QMAX = kMaxSplits / NSLOT;
+    int QG = 1;
+    while (QG < S && QG < NSLOT) QG <<= 1;
+    const int RB = NSLOT / QG;
+    const int rs = tid / L4;  // row slot
+    const int d4 = tid % L4;
+    const int qg = rs % QG;
+    const int rb = rs / QG;
+    float* red_m = reinterpret_cast<float*>(sm.k);
+    float* red_l = red_m + NSLOT;
+    float* red_o = red_l + NSLOT;                            // [NSLOT][D]
+    T* sq = reinterpret_cast<T*>(red_o + NSLOT * D);         // [NSLOT][D] query rows
+    const int v0 = slot_index - it.s * p.n_xcd;              // slot of chunk 0
+    const int moff = p.rows_slot * D;
+    const int loff = moff + p.rows_slot;
+    for (int k0 = 0; it.s + S * k0 < rcount; k0 += RB) {
+      const int r = it.s + S * (k0 + rb);
+      const bool valid = r < rcount;
+      const int rr = rlo + r;
+      float mq[QMAX], lq[QMAX];
+      float4 oq[QMAX];
+#pragma unroll
+      for (int j = 0; j < QMAX; ++j) {
+        const int q = qg + QG * j;
+        if (valid && q < S) {
+          const float* sl = p.partials + size_t(v0 + q * p.n_xcd) * p.slot_floats;
+          mq[j] = sl[moff + r];
+          lq[j] = sl[loff + r];
+          oq[j] = *reinterpret_cast<const float4*>(sl + r * D + 4 * d4);
+        } else {
+          mq[j] = -INFINITY;
+          lq[j] = 0.f;
+          oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      float ms = -INFINITY, ls = 0.f;
+      float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (FUSED) {
+        if (valid && qg == 0) {
+          const T* qrow = static_cast<const T*>(p.q) +
+                          (size_t(si.off + rr / G) * p.hq + it.g * G + rr % G) * D + 4 * d4;
+          if constexpr (kBf16)
+            *reinterpret_cast<uint2*>(sq + rs * D + 4 * d4) = *reinterpret_cast<const uint2*>(qrow);
+          else
+            *reinterpret_cast<uint4*>(sq + rs * D + 4 * d4) = *reinterpret_cast<const uint4*>(qrow);
+        }
+        __syncthreads();
+        if (valid && qg == 0) {
+          TreeSrc<T, D> src{sq + rs * D, sm.tk, sm.tv, D, D, true};
+          tree_row<T, D>(src, si.T, d4, sm.mask[rr / G], p.scale_log2, ms, ls, os);
+        }
+      }
+      float mloc = ms;
+#pragma unroll
+      for (int j = 0; j < QMAX; ++j) mloc = fmaxf(mloc, mq[j]);
+      if (d4 == 0) red_m[rs] = mloc;
+      __syncthreads();
+      float M = -INFINITY;
+      for (int x = 0; x < QG; ++x) M = fmaxf(M, red_m[rb * QG + x]);
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < QMAX; ++j) {
+          const float wq = exp2_fast(mq[j] - M);
+          L = fmaf(wq, lq[j], L);
+          acc.x = fmaf(wq, oq[j].x, acc.x);
+          acc.y = fmaf(wq, oq[j].y, acc.y);
+          acc.z = fmaf(wq, oq[j].z, acc.z);
+          acc.w = fmaf(wq, oq[j].w, acc.w);
+        }
+        if (qg == 0) {
+          const float wsuf = exp2_fast(ms - M);
+          L = fmaf(wsuf, ls, L);
+          acc.x = fmaf(wsuf, os.x, acc.x);
+          acc.y = fmaf(wsuf, os.y, acc.y);
+          acc.z = fmaf(wsuf, os.z, acc.z);
+          acc.w = fmaf(wsuf, os.w, acc.w);
+        }
+      }
+      *reinterpret_cast<float4*>(red_o + rs * D + 4 * d4) = acc;
+      if (d4 == 0) red_l[rs] = L;
+      __syncthreads();
+      if (qg == 0 && valid) {
+        float Lt = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int x = 0; x < QG; ++x) {
+          const int sx = rb * QG + x;
+          Lt += red_l[sx];
+          const float4 ox = *reinterpret_cast<const float4*>(red_o + sx * D + 4 * d4);
+          o.x += ox.x; o.y += ox.y; o.z += ox.z; o.w += ox.w;
+        }
+        float lse = -INFINITY;
+        if (M != -INFINITY) {
+          const float inv = 1.f / Lt;
+          o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+          lse = (M + __log2f(Lt)) * kLn2;
+        } else {
+          o = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const size_t orow = size_t(si.off + rr / G) * p.hq + it.g * G + rr % G;
+        if constexpr (FUSED) {
+          T* dst = static_cast<T*>(p.out) + orow * D + 4 * d4;
+          if constexpr (kBf16) {
+            const uint32_t lo = uint32_t(f32_to_bf16(o.x)) | (uint32_t(f32_to_bf16(o.y)) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(o.z)) | (uint32_t(f32_to_bf16(o.w)) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(dst) = o;
+          }
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * D + 4 * d4) = o;
+        }
+        if (d4 == 0 && p.lse_out) p.lse_out[orow] = lse;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <typename T, int D, bool FUSED, int PD>
+__global__ void __launch_bounds__(kThreads, 1) attn_kernel(Params p) {
+  extern __shared__ int dyn[];  // table numbering: cum[seq_per_xcd + 1], srp[seq_per_xcd]
+  __shared__ Smem<T, D> sm;
+  int* cum = dyn;
+  int2* srp = reinterpret_cast<int2*>(dyn + 2 * ((p.seq_per_xcd + 2) / 2));
+  const int tid = threadIdx.x;
+  const int x = int(blockIdx.x % unsigned(p.n_xcd));
+  if (p.n_xcd > 1 && tid == 0 && xcc_id() != x) set_error(p.hdr, kErrPlacement);
+
+  int items = p.items_per_xcd;
+  if (p.table_mode) {
+    items = build_xcd_table(p, x, cum, srp, sm.scratch);
+  } else if (blockIdx.x == 0) {
+    // validate every sequence once (static numbering reads them lazily)
+    for (int b = tid; b < p.batch; b += kThreads) (void)seq_info(p, b, true);
+    if (tid == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
+      set_error(p.hdr, kErrBadTree);
+  }
+
+  int li = int(blockIdx.x / unsigned(p.n_xcd));
+  while (li < items) {
+    const Item it = decode_item(p, cum, srp, x, li);
+    if (it.valid) process_item<T, D, FUSED, PD>(p, sm, it, li * p.n_xcd + x);
+    __syncthreads();
+    if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket[x], 1u));
+    __syncthreads();
+    li = sm.bcast[0];
+  }
+
+  // the last workgroup to leave resets the counters for the next call
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned n = atomicAdd(&p.hdr->done, 1u);
+    sm.bcast[1] = n == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (sm.bcast[1]) {
+    for (int i = tid; i < p.num_groups; i += kThreads)
+      __hip_atomic_store(p.arrive + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < kMaxXcd)
+      __hip_atomic_store(&p.hdr->ticket[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&p.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ============================================================ mask kernel
+// One wave per sequence: mask_out[off + i] = ancestor-or-self word of node i.
+__global__ void __launch_bounds__(64) mask_kernel(Params p, uint64_t* mask_out) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int o0 = p.tree_offsets[b];
+  const int o1 = p.tree_offsets[b + 1];
+  const int T = o1 - o0;
+  const bool ok = o0 >= 0 && o1 >= o0 && o1 <= p.total_nodes && T <= p.max_tree;
+  if (!ok) {
+    if (lane == 0) set_error(p.hdr, kErrBadTree);
+    return;
+  }
+  if (b == 0 && lane == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
+    set_error(p.hdr, kErrBadTree);
+  bool bad = false;
+  const uint64_t word = tree_mask_wave(p.parents + o0, T, bad);
+  if (bad && lane == 0) set_error(p.hdr, kErrBadTree);
+  if (lane < T) mask_out[o0 + lane] = bad ? 0 : word;
+}
+
+// ========================================================== suffix kernel
+// One workgroup per (sequence, KV head, row pass); D/4 lanes per row, reading
+// q and the tree rows from global memory.  Writes normalised o and natural-log
+// lse of the tree piece.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) suffix_kernel(Params p) {
+  constexpr int L4 = D / 4;
+  constexpr int NSLOT = kThreads / L4;
+  const int grp = blockIdx.x;
+  const int rp = grp % p.rp_max;
+  const int bg = grp / p.rp_max;
+  const int g = bg % p.hkv;
+  const int b = bg / p.hkv;
+  const int o0 = p.tree_offsets[b];
+  const int o1 = p.tree_offsets[b + 1];
+  const int Tn = o1 - o0;
+  if (!(o0 >= 0 && o1 >= o0 && o1 <= p.total_nodes && Tn <= p.max_tree)) return;
+  const int G = p.group;
+  const int R = Tn * G;
+  const int rlo = rp * kRowsPerPass;
+  if (rlo >= R) return;
+  const int rcount = min(kRowsPerPass, R - rlo);
+  const int rs = threadIdx.x / L4;
+  const int d4 = threadIdx.x % L4;
+  for (int r0 = 0; r0 < rcount; r0 += NSLOT) {
+    const int r = r0 + rs;
+    if (r >= rcount) break;
+    const int rr = rlo + r;
+    const uint64_t word = p.mask_in[o0 + rr / G];
+    const size_t orow = size_t(o0 + rr / G) * p.hq + g * G + rr % G;
+    const T* kt = static_cast<const T*>(p.k_tree) + (size_t(o0) * p.hkv + g) * D;
+    const T* vt = static_cast<const T*>(p.v_tree) + (size_t(o0) * p.hkv + g) * D;
+    TreeSrc<T, D> src{static_cast<const T*>(p.q) + orow * D, kt, vt, p.hkv * D, p.hkv * D, false};
+    float m, l;
+    float4 o;
+    tree_row<T, D>(src, Tn, d4, word, p.scale_log2, m, l, o);
+    const bool empty = m == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / l;
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * D + 4 * d4) =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (d4 == 0) p.lse_out[orow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
+  }
+}
+
+// =========================================================== merge kernel
+template <typename OutT>
+__global__ void __launch_bounds__(256) merge_kernel(long long rows, int D, const float* o_a,
+                                                    const float* lse_a, const float* o_b,
+                                                    const float* lse_b, OutT* out, float* lse_out) {
+  const int per_row = D / 4;
+  const long long n = rows * per_row;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const long long r = idx / per_row;
+    const int c = int(idx % per_row) * 4;
+    const float la = lse_a[r], lb = lse_b[r];
+    const float m = fmaxf(la, lb);
+    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = -INFINITY;
+    if (m != -INFINITY) {
+      const float wa = expf(la - m), wb = expf(lb - m);
+      const float tot = wa + wb;
+      const float ca = wa / tot, cb = wb / tot;
+      const float4 a = *reinterpret_cast<const float4*>(o_a + r * D + c);
+      const float4 bb = *reinterpret_cast<const float4*>(o_b + r * D + c);
+      res = make_float4(ca * a.x + cb * bb.x, ca * a.y + cb * bb.y, ca * a.z + cb * bb.z,
+                        ca * a.w + cb * bb.w);
+      lse = m + logf(tot);
+    }
+    OutT* dst = out + r * D + c;
+    dst[0] = Elem<OutT>::from_f(res.x);
+    dst[1] = Elem<OutT>::from_f(res.y);
+    dst[2] = Elem<OutT>::from_f(res.z);
+    dst[3] = Elem<OutT>::from_f(res.w);
+    if (c == 0 && lse_out) lse_out[r] = lse;
+  }
+}
+
+}  // namespace ta
