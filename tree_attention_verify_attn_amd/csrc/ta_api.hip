@@ -89,14 +89,29 @@ int xcd_count() {
 
 const void* attn_kernel_ptr(const ta_shape* s, bool fused);
 
+// LDS bytes for the tree K rows (the same again for tree V) of the fused kernel.
+int tree_lds_half(const ta_shape* s, bool fused) {
+  if (!fused) return 0;
+  const int rowb = s->head_dim * (s->dtype == TA_DTYPE_BF16 ? 2 : 4);
+  return 1024 * cdiv(s->max_tree_nodes * rowb, 1024);
+}
+
+// Dynamic LDS of the attention kernel: tree rows, then the per-XCD item table.
+size_t attn_dyn_lds(const ta_shape* s, bool fused, int table_mode) {
+  size_t bytes = 2 * size_t(tree_lds_half(s, fused));
+  if (table_mode) {
+    const int spx = cdiv(s->batch, xcd_count());
+    bytes += size_t(2 * ((spx + 2) / 2) + 2 * spx) * sizeof(int);
+  }
+  return 16 * ((bytes + 15) / 16);
+}
+
 // Resident prefix-pass workgroups per XCD (bounds the splits of one group).
 int xcd_capacity(const ta_shape* s, bool fused) {
   int cus = device_info().cus;
   if (cus <= 0) return kCusPerXcd;  // no device: assume one workgroup per CU
   const int per_xcd = cus / xcd_count();
-  const int spx = cdiv(s->batch, xcd_count());
-  const size_t dyn = 16 * size_t(cdiv((2 * ((spx + 2) / 2) + 2 * spx) * int(sizeof(int)), 16));
-  return per_xcd * occupancy(attn_kernel_ptr(s, fused), dyn);
+  return per_xcd * occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused, s->batch >= 64));
 }
 
 // Prefix tokens per work item.  Every XCD gets the groups (sequence, KV head,
@@ -191,11 +206,9 @@ int launch_status() {
   return e == hipSuccess ? kOk : kErrHip;
 }
 
-template <typename T> constexpr int pipeline_depth() { return sizeof(T) == 2 ? 4 : 1; }
-
 template <typename T, int D, bool FUSED>
 const void* attn_ptr() {
-  return reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED, pipeline_depth<T>()>);
+  return reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED>);
 }
 
 const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
@@ -208,29 +221,29 @@ const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
 }
 
 template <typename T, int D, bool FUSED>
-int launch_attn(Params p, const WsLayout& L, hipStream_t stream) {
-  constexpr int PD = pipeline_depth<T>();
+int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
   const void* kern = attn_ptr<T, D, FUSED>();
-  const size_t dyn = p.table_mode ? 16 * size_t(cdiv((2 * ((p.seq_per_xcd + 2) / 2) + 2 * p.seq_per_xcd) * int(sizeof(int)), 16)) : 0;
+  p.tree_lds_half = tree_lds_half(s, FUSED);
+  const size_t dyn = attn_dyn_lds(s, FUSED, p.table_mode);
   const int cus = device_info().cus;
   if (cus <= 0) return kErrHip;
   const int cap = (cus / L.n_xcd) * occupancy(kern, dyn);
   int first = L.items_per_xcd < cap ? L.items_per_xcd : cap;
   if (first < 1) first = 1;
   p.first_round = first;
-  hipLaunchKernelGGL((attn_kernel<T, D, FUSED, PD>), dim3(unsigned(first * L.n_xcd)),
-                     dim3(kThreads), dyn, stream, p);
+  hipLaunchKernelGGL((attn_kernel<T, D, FUSED>), dim3(unsigned(first * L.n_xcd)), dim3(kThreads),
+                     dyn, stream, p);
   return launch_status();
 }
 
 template <bool FUSED>
 int dispatch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
   if (s->dtype == TA_DTYPE_BF16) {
-    if (s->head_dim == 128) return launch_attn<uint16_t, 128, FUSED>(p, L, stream);
-    return launch_attn<uint16_t, 64, FUSED>(p, L, stream);
+    if (s->head_dim == 128) return launch_attn<uint16_t, 128, FUSED>(s, p, L, stream);
+    return launch_attn<uint16_t, 64, FUSED>(s, p, L, stream);
   }
-  if (s->head_dim == 128) return launch_attn<float, 128, FUSED>(p, L, stream);
-  return launch_attn<float, 64, FUSED>(p, L, stream);
+  if (s->head_dim == 128) return launch_attn<float, 128, FUSED>(s, p, L, stream);
+  return launch_attn<float, 64, FUSED>(s, p, L, stream);
 }
 
 int check_ws(const ta_shape* s, const WsLayout& L, void* ws, size_t ws_bytes) {

@@ -83,6 +83,7 @@ struct Params {
   int seq_per_xcd;           // table numbering: sequences per XCD (upper bound)
   int items_per_xcd;         // item slots per XCD
   int first_round;           // workgroups per XCD in the grid
+  int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
   float scale_log2;          // softmax_scale * log2(e)
 };
 

@@ -184,7 +184,7 @@ template <typename T, int D>
 struct TreeSrc {
   const T* q;        // this row's query, D elements
   const T* k;        // row j of tree K at k + j * k_stride (chunks XOR-swizzled if swz)
-  const T* v;        // row j of tree V at v + j * v_stride
+  const T* v;        // row j of tree V at v + j * v_stride (swizzled like k)
   int k_stride, v_stride;
   bool swz;
 };
@@ -241,7 +241,11 @@ __device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word
 #pragma unroll
     for (int k = 1; k < KPL; ++k) mine = (jj / L4 == k) ? pk[k] : mine;
     const float pj = __shfl(mine, jj % L4, L4);
-    const T* vrow = src.v + size_t(jj) * src.v_stride + 4 * d4;
+    // element 4*d4 sits in 16-byte chunk (4*d4*sizeof(T))/16 of the row
+    constexpr int EPC = 16 / int(sizeof(T));  // elements per chunk
+    const int vc = (4 * d4) / EPC;
+    const int vcs = src.swz ? (vc ^ (jj & SWZ)) : vc;
+    const T* vrow = src.v + size_t(jj) * src.v_stride + vcs * EPC + (4 * d4) % EPC;
     float v[4];
     if constexpr (sizeof(T) == 2) {
       const uint2 raw = *reinterpret_cast<const uint2*>(vrow);
@@ -261,65 +265,93 @@ __device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word
 }
 
 // =========================================================== prefix piece
+// LDS of one workgroup.  The two KV ring slots are separate __shared__ objects
+// (declared in attn_kernel) so that reads of one slot are not ordered behind
+// the still-running DMA into the other.
 template <typename T, int D>
-struct Smem {
-  static constexpr int KCH = D * int(sizeof(T)) / 16;  // 16-byte chunks per K row
-  static constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
-  static constexpr int VP = kBlock + 4;                // V^T row pitch (elements)
-  alignas(16) unsigned char k[kBlock * KCH * 16];      // K block / combine scratch
-  alignas(16) T vt[D * VP];                            // V block transposed
-  alignas(16) T tk[kMaxTree * D];                      // tree K rows (swizzled chunks)
-  alignas(16) T tv[kMaxTree * D];                      // tree V rows
+struct Geo {
+  static constexpr int ROWB = D * int(sizeof(T));          // bytes per K/V row
+  static constexpr int KCH = ROWB / 16;                    // 16-byte chunks per row
+  static constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;    // XOR swizzle of chunk index
+  static constexpr int BLKB = kBlock * ROWB;               // bytes of one K (or V) block
+  static constexpr int KI = BLKB / (kWaves * 1024);        // DMA instructions per wave per tensor
+  static constexpr int QCH = D / 4 * int(sizeof(T)) / 16;  // 16-byte chunks of the Q fragment
+  static constexpr int DT = D / 16;                        // 16-wide head-dim tiles of O^T
+  static constexpr int NS = sizeof(T) == 2 ? 2 : 1;        // KV ring slots
+};
+
+struct SmemMisc {
   uint64_t mask[kMaxTree];
   int scratch[kThreads];
   int bcast[4];
 };
 
-template <typename T> struct VLoad;                // per-lane bytes of one V row
-template <> struct VLoad<uint16_t> { using d64 = uint16_t; using d128 = uint32_t; };
-template <> struct VLoad<float> { using d64 = float; using d128 = uint2; };
-
-template <typename T, int D> struct Traits {
-  static constexpr int KCH = D * int(sizeof(T)) / 16;
-  static constexpr int KPT = kBlock * KCH / kThreads;     // K chunks per thread per block
-  static constexpr int TPT = kMaxTree * KCH / kThreads;   // tree-row chunks per thread
-  static constexpr int DPL = D / 64;                      // head-dim elements per lane in V rows
-  using VT = typename std::conditional<D == 64, typename VLoad<T>::d64,
-                                       typename VLoad<T>::d128>::type;
-  static constexpr int QCH = D / 4 * int(sizeof(T)) / 16; // 16-byte chunks of the Q fragment
-  static constexpr int DT = D / 16;                       // 16-wide head-dim tiles of O^T
-};
-
-// element e (0..DPL-1) of one staged V word, as raw bits
+// byte offset of logical 16-byte chunk c of row t in a swizzled row-major tile
 template <typename T, int D>
-__device__ __forceinline__ uint32_t v_elem(typename Traits<T, D>::VT w, int e) {
-  if constexpr (sizeof(T) == 2) {
-    if constexpr (D == 64) return w;
-    else return e == 0 ? (w & 0xffffu) : (w >> 16);
-  } else {
-    if constexpr (D == 64) return __builtin_bit_cast(uint32_t, w);
-    else return e == 0 ? w.x : w.y;
+__device__ __forceinline__ int swz_off(int t, int c) {
+  using Gm = Geo<T, D>;
+  return t * Gm::ROWB + ((c ^ (t & Gm::SWZ)) << 4);
+}
+
+// One 16-byte global -> LDS transfer per lane: the lane's 16 bytes from g land
+// at lds_base + 16 * lane (lds_base is wave-uniform).  The address-space cast
+// exists only for the device target, so the host pass sees an empty body.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#endif
+}
+
+// Transposing 64-bit LDS read of 16-bit elements (ds_read_b64_tr_b16): inside
+// each group of 16 lanes, lane L receives element L of the 4 rows whose
+// addresses lanes 4j..4j+3 supply (j = 0..3), i.e. a 4x16 -> 16x4 transpose.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<unsigned char*>(a)));
+  return __builtin_bit_cast(uint2, r);
+#else
+  (void)a;
+  return uint2{0, 0};
+#endif
+}
+
+// DMA one 64-token K or V block (64 x D, row-major, swizzled) into LDS.
+template <typename T, int D>
+__device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char* lds) {
+  using Gm = Geo<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < Gm::KI; ++i) {
+    const int u = (w * Gm::KI + i) * 64 + lane;  // LDS chunk this lane fills
+    const int t = u / Gm::KCH;
+    const int pc = u % Gm::KCH;
+    const int c = pc ^ (t & Gm::SWZ);
+    lds_dma16(g + t * Gm::ROWB + c * 16, lds + (w * Gm::KI + i) * 1024);
   }
 }
 
-template <typename T, int D, bool FUSED, int PD>
-__device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, int slot_index) {
-  const int lane0 = threadIdx.x & 63;
-  // block ids of the chunk (lane j: block j) and the sequence's facts, read in
-  // one round trip; ids past the sequence's prefix are never used
-  int my_id = -1;
-  {
-    const int lb = it.s * (p.chunk / kBlock) + lane0;
-    if (lane0 < p.chunk / kBlock && lb < p.max_blocks)
-      my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
-  }
-  const SeqInfo si = seq_info(p, it.b, false);
-  if (it.rp >= si.RP || it.s >= si.S) return;  // static numbering: no such item
-  using Tr = Traits<T, D>;
-  using VT = typename Tr::VT;
-  constexpr int KCH = Tr::KCH, KPT = Tr::KPT, TPT = Tr::TPT, DPL = Tr::DPL, QCH = Tr::QCH,
-                DT = Tr::DT;
-  constexpr int VP = Smem<T, D>::VP, SWZ = Smem<T, D>::SWZ;
+// Wait until at most n of this wave's vector-memory operations are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+// Barrier that does not drain outstanding loads (the caller waits for what it needs).
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_s_waitcnt((0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+  __asm__ __volatile__("s_barrier" ::: "memory");
+}
+
+template <typename T, int D, bool FUSED>
+__device__ void process_item(const Params& p, unsigned char* slot0, unsigned char* slot1,
+                             unsigned char* tree_lds, SmemMisc& sm, const Item& it,
+                             int slot_index) {
+  using Gm = Geo<T, D>;
+  constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, SWZ = Gm::SWZ, BLKB = Gm::BLKB, KI = Gm::KI,
+                QCH = Gm::QCH, DT = Gm::DT, NS = Gm::NS;
   constexpr bool kBf16 = sizeof(T) == 2;
 
   const int tid = threadIdx.x;
@@ -327,6 +359,17 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
   const int w = tid >> 6;
   const int lr = lane & 15;
   const int kq = lane >> 4;
+
+  // block ids of the chunk (lane j: block j) and the sequence's facts, read in
+  // one round trip; ids past the sequence's prefix are never used
+  int my_id = -1;
+  {
+    const int lb = it.s * (p.chunk / kBlock) + lane;
+    if (lane < p.chunk / kBlock && lb < p.max_blocks)
+      my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
+  }
+  const SeqInfo si = seq_info(p, it.b, false);
+  if (it.rp >= si.RP || it.s >= si.S) return;  // static numbering: no such item
 
   const int G = p.group;
   const int R = si.T * G;
@@ -337,86 +380,36 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
   const int ntok = max(0, min(si.P, t0 + p.chunk) - t0);
   const int nblk = cdiv(ntok, kBlock);
   const int S = si.S;
-
-
-  uint4 kreg[PD][KPT];
-  VT vreg[PD][16];
-  int nv[PD];
   const size_t head_stride = size_t(kBlock) * D;  // elements per (block, head)
-  auto issue = [&](int st, int j) {
-    int id = __shfl(my_id, j);
-    const bool ok = id >= 0 && id < p.num_blocks;
-    if (!ok) {
-      if (tid == 0) set_error(p.hdr, kErrBadPrefix);
-      id = 0;
-    }
-    nv[st] = ok ? min(kBlock, ntok - j * kBlock) : 0;
-    const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
-    const unsigned char* kb = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base);
-    const unsigned char* vb = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      kreg[st][i] = *reinterpret_cast<const uint4*>(kb + size_t(i * kThreads + tid) * 16);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      vreg[st][k] = *reinterpret_cast<const VT*>(vb + (size_t(16 * w + k) * D + lane * DPL) * sizeof(T));
-  };
-  auto store = [&](int st) {
-    const int nvalid = nv[st];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = i * kThreads + tid;
-      const int tok = u / KCH;
-      const int c = u % KCH;
-      const uint4 val = tok < nvalid ? kreg[st][i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(sm.k + (tok * KCH + (c ^ (tok & SWZ))) * 16) = val;
-    }
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        uint32_t xv[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int tok = 16 * w + 4 * gi + tt;
-          xv[tt] = tok < nvalid ? v_elem<T, D>(vreg[st][4 * gi + tt], e) : 0u;
-        }
-        T* dst = sm.vt + (lane * DPL + e) * VP + 16 * w + 4 * gi;
-        if constexpr (kBf16) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(xv[0] | (xv[1] << 16), xv[2] | (xv[3] << 16));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(xv[0], xv[1], xv[2], xv[3]);
-        }
-      }
-    }
-  };
 
-  // ---- issue the first PD blocks
-#pragma unroll
-  for (int st = 0; st < PD; ++st)
-    if (st < nblk) issue(st, st);
-
-  // ---- tree rows and parents of (b, g) (fused): loaded now, staged into LDS
-  // with the first block.  Addresses are clamped to row T-1 so every load is
-  // unconditional and in bounds.
-  uint4 tkr[FUSED ? TPT : 1], tvr[FUSED ? TPT : 1];
+  // ---- tree rows (fused, chunk 0 of the group only: that chunk also attends
+  // to the tree): DMA into LDS, issued before the KV blocks so that waiting
+  // for them does not wait for the blocks.  Every staged row past the tree
+  // holds a copy of its last node, so all staged rows are finite.
+  unsigned char* tk = tree_lds;
+  unsigned char* tv = tree_lds + p.tree_lds_half;
+  const int tree_rows = p.tree_lds_half / ROWB;  // staged rows (>= tree size)
+  const bool with_tree = FUSED && it.s == 0;
   int par = -1;
-  if constexpr (FUSED) {
+  if (with_tree) {
     const int Tn = si.T;
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int u = i * kThreads + tid;
-      const int row = min(u / KCH, Tn - 1);
-      const int c = u % KCH;
-      const size_t roff = (size_t(si.off + row) * p.hkv + it.g) * D;
-      tkr[i] = reinterpret_cast<const uint4*>(static_cast<const T*>(p.k_tree) + roff)[c];
-      tvr[i] = reinterpret_cast<const uint4*>(static_cast<const T*>(p.v_tree) + roff)[c];
+    const int ninstr = p.tree_lds_half / 1024;
+    for (int m = w; m < ninstr; m += kWaves) {
+      const int u = m * 64 + lane;
+      const int t = min(u / KCH, Tn - 1);
+      const int pc = u % KCH;
+      const int c = pc ^ ((u / KCH) & SWZ);
+      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+      const unsigned char* gk = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff);
+      const unsigned char* gv = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff);
+      lds_dma16(gk + c * 16, tk + m * 1024);
+      lds_dma16(gv + c * 16, tv + m * 1024);
     }
     if (w == 0) par = p.parents[si.off + min(lane, Tn - 1)];
   }
 
   // ---- Q fragment of this wave's row tile: lane (row lr, group kq) holds the
-  // contiguous head-dim range [kq*D/4, (kq+1)*D/4) of its row.
+  // contiguous head-dim range [kq*D/4, (kq+1)*D/4) of its row
   const bool active = w < RT;
   uint4 qv[QCH];
   {
@@ -434,61 +427,94 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
     }
   }
 
-  auto stage_tree = [&]() {
-    if constexpr (FUSED) {
-      const int Tn = si.T;
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int u = i * kThreads + tid;
-        const int row = u / KCH;
-        const int c = u % KCH;
-        if (row < Tn) {
-          reinterpret_cast<uint4*>(sm.tk + row * D)[c ^ (row & SWZ)] = tkr[i];
-          reinterpret_cast<uint4*>(sm.tv + row * D)[c] = tvr[i];
-        }
-      }
-      if (w == 0) {
-        // ancestor-or-self words by pointer jumping (as in tree_mask_wave)
-        const bool bad_lane = lane < Tn && !(par == -1 || (par >= 0 && par < lane));
-        int up = (lane < Tn && !bad_lane) ? par : -1;
-        uint64_t anc = lane < Tn ? (uint64_t(1) << lane) : 0;
-#pragma unroll
-        for (int round = 0; round < 6; ++round) {
-          const int src = up >= 0 ? up : lane;
-          const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src);
-          const uint32_t hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
-          const int up2 = __shfl(up, src);
-          if (up >= 0) {
-            anc |= (static_cast<uint64_t>(hi) << 32) | lo;
-            up = up2;
-          }
-        }
-        sm.mask[lane] = anc;
-        if (__any(bad_lane) && lane == 0 && it.s == 0 && it.g == 0 && it.rp == 0)
-          set_error(p.hdr, kErrBadTree);
-      }
+  // ---- KV blocks -> LDS ring
+  auto block_src = [&](int j, int& nvalid) -> size_t {
+    int id = __shfl(my_id, j);
+    const bool ok = id >= 0 && id < p.num_blocks;
+    if (!ok) {
+      if (tid == 0) set_error(p.hdr, kErrBadPrefix);
+      id = 0;
     }
+    nvalid = ok ? min(kBlock, ntok - j * kBlock) : 0;
+    return (size_t(id) * p.hkv + it.g) * head_stride;
   };
+  int nv0 = 0, nv1 = 0;
+  auto issue = [&](int j, unsigned char* slot, int& nv) {
+    const size_t base = block_src(j, nv);
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot);
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB);
+  };
+  if (nblk > 0) issue(0, slot0, nv0);
+  if constexpr (NS == 2) {
+    if (nblk > 1) issue(1, slot1, nv1);
+  }
+
+  // ---- tree staging: wait for the tree DMA and parents (older than the
+  // blocks), then the tree mask by pointer jumping (as in tree_mask_wave)
+  if (with_tree) {
+    if constexpr (NS == 2) {
+      if (nblk > 1) wait_vm<4 * KI>();
+      else if (nblk == 1) wait_vm<2 * KI>();
+      else wait_vm<0>();
+    } else {
+      if (nblk > 0) wait_vm<2 * KI>();
+      else wait_vm<0>();
+    }
+    if (w == 0) {
+      const int Tn = si.T;
+      const bool bad_lane = lane < Tn && !(par == -1 || (par >= 0 && par < lane));
+      int up = (lane < Tn && !bad_lane) ? par : -1;
+      uint64_t anc = lane < Tn ? (uint64_t(1) << lane) : 0;
+#pragma unroll
+      for (int round = 0; round < 6; ++round) {
+        const int src = up >= 0 ? up : lane;
+        const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src);
+        const uint32_t hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+        const int up2 = __shfl(up, src);
+        if (up >= 0) {
+          anc |= (static_cast<uint64_t>(hi) << 32) | lo;
+          up = up2;
+        }
+      }
+      sm.mask[lane] = anc;
+      if (__any(bad_lane) && lane == 0 && it.s == 0 && it.g == 0 && it.rp == 0)
+        set_error(p.hdr, kErrBadTree);
+    }
+  }
 
   float m_run = -INFINITY, l_run = 0.f;
   floatx4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int nvalid) {
-    // every LDS read of the block is issued before the MFMAs that consume it,
-    // so the reads overlap instead of each waiting its own round trip
+  // zero the V rows past the prefix in a partial block (the cache may hold
+  // anything there, and 0 * NaN would leak into the PV product)
+  auto clear_tail = [&](unsigned char* slot, int nvalid) {
+    unsigned char* vb = slot + BLKB;
+    for (int u = tid; u < (kBlock - nvalid) * KCH; u += kThreads) {
+      const int t = nvalid + u / KCH;
+      *reinterpret_cast<uint4*>(vb + swz_off<T, D>(t, u % KCH)) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // One 64-key block: a prefix block (keys < nvalid visible) or, with
+  // kTree, the staged tree rows (key j visible to a row iff bit j of its
+  // node's mask word is set; staged-row reads are clamped to the staging area).
+  auto compute = [&](auto tree_tag, const unsigned char* kb, const unsigned char* vb, int nvalid) {
+    constexpr bool kTree = decltype(tree_tag)::value;
+    auto krow = [&](int t) { return kTree ? min(t, tree_rows - 1) : t; };
+    uint64_t word = 0;
+    if constexpr (kTree) {
+      const int r = 16 * w + lr;
+      word = r < rcount ? sm.mask[(rlo + r) / G] : 0;
+    }
+    // every LDS read is issued before the MFMAs that consume it
     uint4 kf[4][QCH];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 16 * tt + lr;
-      const unsigned char* krow = sm.k + tok * KCH * 16;
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int c = 0; c < QCH; ++c) {
-        const int lc = kq * QCH + c;  // logical 16-byte chunk of the K row
-        kf[tt][c] = *reinterpret_cast<const uint4*>(krow + ((lc ^ (tok & SWZ)) * 16));
-      }
-    }
+      for (int c = 0; c < QCH; ++c)
+        kf[tt][c] = *reinterpret_cast<const uint4*>(kb + swz_off<T, D>(krow(16 * tt + lr), kq * QCH + c));
     floatx4 sacc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -511,20 +537,25 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
             sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[tt], 0, 0, 0);
         }
       }
-    // V^T fragments for the PV product, read while the softmax runs
-    constexpr int NVF = kBf16 ? 2 * DT : 4 * DT;
+    // V^T fragments (A operand of O^T += V^T P^T), read while the softmax runs.
+    // bf16: the LDS transpose read gives lane (d, group kq) four consecutive
+    // tokens of column d; two of them make the eight k-slots of the MFMA.
+    constexpr int NVF = kBf16 ? 2 * DT : 1;
     uint4 vf[NVF];
+    if constexpr (kBf16) {
+      const int L = lane & 15;
 #pragma unroll
-    for (int f = 0; f < NVF; ++f) {
-      if constexpr (kBf16) {
+      for (int f = 0; f < NVF; ++f) {
         const int kk = f / DT, dt = f % DT;
-        const T* vrow = sm.vt + (16 * dt + lr) * VP + 32 * kk + 4 * kq;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        vf[f] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        const int tt = f / DT, dt = f % DT;
-        vf[f] = *reinterpret_cast<const uint4*>(sm.vt + (16 * dt + lr) * VP + 16 * tt + 4 * kq);
+        uint2 half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = krow(32 * kk + 16 * h + 4 * kq + (L >> 2));
+          const int cb = 32 * dt + 8 * (L & 3);  // byte column
+          const unsigned char* a = vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15);
+          half[h] = lds_read_tr16(a);
+        }
+        vf[f] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
       }
     }
     // lane (row lr, group kq) holds tokens 16*tt + 4*kq + i of its row
@@ -535,7 +566,8 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * tt + 4 * kq + i;
-        sc[tt][i] = tok < nvalid ? sacc[tt][i] * p.scale_log2 : -INFINITY;
+        const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
+        sc[tt][i] = vis ? sacc[tt][i] * p.scale_log2 : -INFINITY;
         bmax = fmaxf(bmax, sc[tt][i]);
       }
     bmax = max_over_quads(bmax);
@@ -555,8 +587,9 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float e = exp2_fast(sc[tt][i] - m_use);
-        if constexpr (kBf16) e = bf16_to_f32(f32_to_bf16(e));  // the value the MFMA sees
+        // the denominator takes the fp32 weight, so the row's lse is exact to
+        // fp32 rounding; only the PV operand is rounded to bf16
+        const float e = exp2_fast(sc[tt][i] - m_use);
         pr[tt][i] = e;
         rsum += e;
       }
@@ -578,49 +611,68 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
               __builtin_bit_cast(bf16x8, vf[kk * DT + dt]), bp, oacc[dt], 0, 0, 0);
       }
     } else {
+      // fp32: A operand V^T[16dt + lr][16tt + 4kq + i], one element per MFMA
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint4 a = vf[tt * DT + dt];
-          const float av[4] = {__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y),
-                               __builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w)};
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], pr[tt][i], oacc[dt], 0, 0, 0);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int row = krow(16 * tt + 4 * kq + i);
+            const int cb = (16 * dt + lr) * 4;
+            const float a = *reinterpret_cast<const float*>(
+                vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, pr[tt][i], oacc[dt], 0, 0, 0);
+          }
     }
   };
 
-  // ---- stream the chunk: PD blocks in flight, one block resident in LDS
-  if (nblk == 0) stage_tree();
-  for (int jb = 0; jb < nblk; jb += PD) {
-#pragma unroll
-    for (int st = 0; st < PD; ++st) {
-      const int j = jb + st;
-      if (j < nblk) {
-        __syncthreads();  // everyone is done reading the previous block
-        store(st);
-        if (j == 0) stage_tree();
-        const int nvalid = nv[st];
-        if (j + PD < nblk) issue(st, j + PD);
-        __syncthreads();
-        if (active) compute(nvalid);
-      }
-    }
+  // ---- the tree piece, while the first KV blocks are still in flight
+  if (with_tree) {
+    raw_barrier();  // staged rows of every wave and the mask words are in LDS
+    if (active) compute(std::true_type{}, tk, tv, 0);
   }
 
+  // ---- stream the chunk through the ring: block j sits in slot j % NS; the
+  // DMA of block j + NS starts as soon as every wave is done with block j
+  auto step = [&](int j, unsigned char* slot, int& nv) {
+    const bool more = j + 1 < nblk;  // is a later block in flight?
+    if constexpr (NS == 2) {
+      if (more) wait_vm<2 * KI>(); else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    raw_barrier();
+    if (nv < kBlock) {
+      clear_tail(slot, nv);
+      raw_barrier();
+    }
+    if (active) compute(std::false_type{}, slot, slot + BLKB, nv);
+    raw_barrier();
+    if (j + NS < nblk) issue(j + NS, slot, nv);
+  };
+  if constexpr (NS == 2) {
+    for (int j = 0; j < nblk; j += 2) {
+      step(j, slot0, nv0);
+      if (j + 1 < nblk) step(j + 1, slot1, nv1);
+    }
+  } else {
+    for (int j = 0; j < nblk; ++j) step(j, slot0, nv0);
+  }
+  wait_vm<0>();
+  __syncthreads();
+
   // ---- chunk partial -> workspace (plain stores: read back in this XCD's L2)
-  float* slot = p.partials + size_t(slot_index) * p.slot_floats;
+  float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
   if (active) {
     const int r = 16 * w + lr;
     if (r < rcount) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<floatx4*>(slot + r * D + 16 * dt + 4 * kq) = oacc[dt];
+        *reinterpret_cast<floatx4*>(slotp + r * D + 16 * dt + 4 * kq) = oacc[dt];
       if (kq == 0) {
-        slot[p.rows_slot * D + r] = m_run;
-        slot[p.rows_slot * D + p.rows_slot + r] = l_run;
+        slotp[p.rows_slot * D + r] = m_run;
+        slotp[p.rows_slot * D + p.rows_slot + r] = l_run;
       }
     }
   }
@@ -650,8 +702,9 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
   // ---- combine.  The S items of the group share its rows: item s takes rows
   // s, s + S, ...  For one row, D/4 lanes (a row slot) cover the head dim, 4
   // elements each; QG row slots split the S chunk partials between them (all
-  // loads issued up front), then meet in LDS.  Chunk partials and, in the fused
-  // kernel, the row's tree piece are folded with their log-sum-exp weights.
+  // loads issued up front), then meet in LDS.  The chunk partials (in the fused
+  // kernel chunk 0's also holds the tree piece) are folded with their
+  // log-sum-exp weights.
   // [merge_attentions over disjoint KV chunks: pith.science verdict record,
   // pith_extraction.supporting_citations (Juravsky et al. 2024)]
   {
@@ -665,10 +718,9 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
     const int d4 = tid % L4;
     const int qg = rs % QG;
     const int rb = rs / QG;
-    float* red_m = reinterpret_cast<float*>(sm.k);
+    float* red_m = reinterpret_cast<float*>(slot0);
     float* red_l = red_m + NSLOT;
     float* red_o = red_l + NSLOT;                            // [NSLOT][D]
-    T* sq = reinterpret_cast<T*>(red_o + NSLOT * D);         // [NSLOT][D] query rows
     const int v0 = slot_index - it.s * p.n_xcd;              // slot of chunk 0
     const int moff = p.rows_slot * D;
     const int loff = moff + p.rows_slot;
@@ -692,24 +744,7 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
           oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
-      float ms = -INFINITY, ls = 0.f;
-      float4 os = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (FUSED) {
-        if (valid && qg == 0) {
-          const T* qrow = static_cast<const T*>(p.q) +
-                          (size_t(si.off + rr / G) * p.hq + it.g * G + rr % G) * D + 4 * d4;
-          if constexpr (kBf16)
-            *reinterpret_cast<uint2*>(sq + rs * D + 4 * d4) = *reinterpret_cast<const uint2*>(qrow);
-          else
-            *reinterpret_cast<uint4*>(sq + rs * D + 4 * d4) = *reinterpret_cast<const uint4*>(qrow);
-        }
-        __syncthreads();
-        if (valid && qg == 0) {
-          TreeSrc<T, D> src{sq + rs * D, sm.tk, sm.tv, D, D, true};
-          tree_row<T, D>(src, si.T, d4, sm.mask[rr / G], p.scale_log2, ms, ls, os);
-        }
-      }
-      float mloc = ms;
+      float mloc = -INFINITY;
 #pragma unroll
       for (int j = 0; j < QMAX; ++j) mloc = fmaxf(mloc, mq[j]);
       if (d4 == 0) red_m[rs] = mloc;
@@ -727,14 +762,6 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
           acc.y = fmaf(wq, oq[j].y, acc.y);
           acc.z = fmaf(wq, oq[j].z, acc.z);
           acc.w = fmaf(wq, oq[j].w, acc.w);
-        }
-        if (qg == 0) {
-          const float wsuf = exp2_fast(ms - M);
-          L = fmaf(wsuf, ls, L);
-          acc.x = fmaf(wsuf, os.x, acc.x);
-          acc.y = fmaf(wsuf, os.y, acc.y);
-          acc.z = fmaf(wsuf, os.z, acc.z);
-          acc.w = fmaf(wsuf, os.w, acc.w);
         }
       }
       *reinterpret_cast<float4*>(red_o + rs * D + 4 * d4) = acc;
@@ -777,12 +804,16 @@ __device__ void process_item(const Params& p, Smem<T, D>& sm, const Item& it, in
   }
 }
 
-template <typename T, int D, bool FUSED, int PD>
-__global__ void __launch_bounds__(kThreads, 1) attn_kernel(Params p) {
-  extern __shared__ int dyn[];  // table numbering: cum[seq_per_xcd + 1], srp[seq_per_xcd]
-  __shared__ Smem<T, D> sm;
-  int* cum = dyn;
-  int2* srp = reinterpret_cast<int2*>(dyn + 2 * ((p.seq_per_xcd + 2) / 2));
+template <typename T, int D, bool FUSED>
+__global__ void __launch_bounds__(kThreads, 2) attn_kernel(Params p) {
+  using Gm = Geo<T, D>;
+  extern __shared__ __attribute__((aligned(16))) int dyn[];  // tree rows, then the item table
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * Gm::BLKB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[Gm::NS == 2 ? 2 * Gm::BLKB : 16];
+  __shared__ SmemMisc sm;
+  unsigned char* tree_lds = reinterpret_cast<unsigned char*>(dyn);
+  int* cum = dyn + p.tree_lds_half / 2;  // after 2 * tree_lds_half bytes
+  int2* srp = reinterpret_cast<int2*>(cum + 2 * ((p.seq_per_xcd + 2) / 2));
   const int tid = threadIdx.x;
   const int x = int(blockIdx.x % unsigned(p.n_xcd));
   if (p.n_xcd > 1 && tid == 0 && xcc_id() != x) set_error(p.hdr, kErrPlacement);
@@ -800,7 +831,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(Params p) {
   int li = int(blockIdx.x / unsigned(p.n_xcd));
   while (li < items) {
     const Item it = decode_item(p, cum, srp, x, li);
-    if (it.valid) process_item<T, D, FUSED, PD>(p, sm, it, li * p.n_xcd + x);
+    if (it.valid) process_item<T, D, FUSED>(p, ring0, ring1, tree_lds, sm, it, li * p.n_xcd + x);
     __syncthreads();
     if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket[x], 1u));
     __syncthreads();
