@@ -80,9 +80,7 @@ typedef enum {
   TA_ERR_WORKSPACE = 4,    /* workspace null or smaller than tree_attn_workspace_size */
   TA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
   TA_ERR_BAD_PREFIX = 6,   /* device-detected: prefix length or block id out of range */
-  TA_ERR_TIMEOUT = 7,      /* device-detected: a bounded cross-workgroup wait gave up */
-  TA_ERR_PLACEMENT = 8     /* device-detected: a workgroup ran on another XCD than the
-                              round-robin placement the work split relies on */
+  TA_ERR_TIMEOUT = 7       /* device-detected: a bounded cross-workgroup wait gave up */
 } ta_status;
 
 typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
@@ -90,7 +88,7 @@ typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
 /* Host-side description of one call.  Everything here is a host value; the
  * per-sequence data (prefix lengths, trees) stays on the device. */
 typedef struct {
-  int32_t batch;              /* B >= 1 (B <= 4096) */
+  int32_t batch;              /* B >= 1 (B <= 2048) */
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* D in {64, 128} */
@@ -109,8 +107,10 @@ typedef struct {
 /* Bytes of device workspace tree_attn_prefix / tree_attn_verify /
  * tree_attn_build_mask need for `shape` (0 if the shape is invalid).
  * A workspace must be zero-filled before its first use (tree_attn_workspace_init
- * does that); every call that returns TA_OK leaves its counters zeroed again,
- * so the same workspace can be reused call after call on one stream. */
+ * does that).  A call that completes without a device-detected error leaves
+ * the workspace's counters ready for the next call, so one workspace serves
+ * call after call on one stream; after TA_ERR_TIMEOUT it must be zero-filled
+ * again. */
 size_t tree_attn_workspace_size(const ta_shape* shape);
 
 /* Zero-fill a workspace with a kernel (no hipMemset, so graph capture is safe). */

@@ -43,10 +43,11 @@ int occupancy(const void* kernel, size_t dyn) {
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
+  // 0 when the launch does not fit a CU (too much LDS)
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, dyn) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kAttnThreads, dyn) != hipSuccess)
     occ = 1;
-  if (occ < 1) occ = 1;
+  if (occ < 0) occ = 0;
   cache[key] = occ;
   return occ;
 }
@@ -77,16 +78,6 @@ int check_shape(const ta_shape* s) {
 
 int group_of(const ta_shape* s) { return s->num_q_heads / s->num_kv_heads; }
 
-// XCDs of the current device (gfx950: 32 CUs each); 8 when no device is visible.
-int xcd_count() {
-  int cus = device_info().cus;
-  if (cus <= 0) cus = 8 * kCusPerXcd;
-  int n = cus / kCusPerXcd;
-  if (n < 1) n = 1;
-  if (n > kMaxXcd) n = kMaxXcd;
-  return n;
-}
-
 const void* attn_kernel_ptr(const ta_shape* s, bool fused);
 
 // LDS bytes for the tree K rows (the same again for tree V) of the fused kernel.
@@ -99,19 +90,16 @@ int tree_lds_half(const ta_shape* s, bool fused) {
 // Dynamic LDS of the attention kernel: tree rows, then the per-XCD item table.
 size_t attn_dyn_lds(const ta_shape* s, bool fused, int table_mode) {
   size_t bytes = 2 * size_t(tree_lds_half(s, fused));
-  if (table_mode) {
-    const int spx = cdiv(s->batch, xcd_count());
-    bytes += size_t(2 * ((spx + 2) / 2) + 2 * spx) * sizeof(int);
-  }
+  if (table_mode) bytes += size_t(2 * s->batch + 1) * sizeof(int);  // cum[B + 1], srp[B]
   return 16 * ((bytes + 15) / 16);
 }
 
 // Resident prefix-pass workgroups per XCD (bounds the splits of one group).
-int xcd_capacity(const ta_shape* s, bool fused) {
+int grid_capacity(const ta_shape* s, bool fused) {
   int cus = device_info().cus;
-  if (cus <= 0) return kCusPerXcd;  // no device: assume one workgroup per CU
-  const int per_xcd = cus / xcd_count();
-  return per_xcd * occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused, s->batch >= 64));
+  if (cus <= 0) cus = 256;  // no device: size for a full MI355X, one workgroup per CU
+  const int occ = occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused, s->batch >= kTableBatch));
+  return cus * (occ > 0 ? occ : 1);
 }
 
 // Prefix tokens per work item.  Every XCD gets the groups (sequence, KV head,
@@ -121,7 +109,7 @@ int xcd_capacity(const ta_shape* s, bool fused) {
 // wait for each other) nor more than kMaxSplits.
 int choose_chunk(const ta_shape* s, bool fused) {
   const int P = s->max_prefix_len > 0 ? s->max_prefix_len : 1;
-  const int cap = xcd_capacity(s, fused);
+  const int cap = grid_capacity(s, fused);
   const int max_splits = cap < kMaxSplits ? cap : kMaxSplits;
   const int min_chunk = kBlock * cdiv(cdiv(P, max_splits), kBlock);
   int chunk;
@@ -131,8 +119,7 @@ int choose_chunk(const ta_shape* s, bool fused) {
     const int G = group_of(s);
     const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
                              cdiv(s->max_tree_nodes * G, kRowsPerPass);
-    const long long per_xcd = (groups + xcd_count() - 1) / xcd_count();
-    const long long tok = (per_xcd * P + cap - 1) / cap;
+    const long long tok = (groups * P + cap - 1) / cap;
     chunk = static_cast<int>(kBlock * ((tok + kBlock - 1) / kBlock));
   }
   if (chunk < kBlock) chunk = kBlock;
@@ -146,7 +133,6 @@ WsLayout layout_for(const ta_shape* s, int chunk) {
   const int G = group_of(s);
   const int D = s->head_dim;
   L.chunk = chunk;
-  L.n_xcd = xcd_count();
   L.rp_max = cdiv(s->max_tree_nodes * G, kRowsPerPass);
   int rows = s->max_tree_nodes * G;
   if (rows > kRowsPerPass) rows = kRowsPerPass;
@@ -155,15 +141,12 @@ WsLayout layout_for(const ta_shape* s, int chunk) {
   L.num_groups = s->batch * s->num_kv_heads * L.rp_max;
   L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
   // large batches: dense per-XCD numbering from a prefix table; small: static
-  L.table_mode = s->batch >= 64 ? 1 : 0;
-  L.lg_per_xcd = cdiv(L.num_groups, L.n_xcd);
-  L.seq_per_xcd = cdiv(s->batch, L.n_xcd);
-  L.items_per_xcd = L.table_mode ? L.seq_per_xcd * s->num_kv_heads * L.rp_max * L.s_max
-                                 : L.lg_per_xcd * L.s_max;
+  L.table_mode = s->batch >= kTableBatch ? 1 : 0;
+  L.item_slots = L.num_groups * L.s_max;
   L.arrive_off = sizeof(WsHeader);
-  L.partial_off = align256(L.arrive_off + sizeof(unsigned) * size_t(L.num_groups));
+  L.partial_off = align256(L.arrive_off + sizeof(unsigned) * kCounterStride * size_t(L.num_groups));
   L.total = L.partial_off +
-            size_t(L.n_xcd) * size_t(L.items_per_xcd) * L.slot_floats * sizeof(float);
+            size_t(L.item_slots) * L.slot_floats * sizeof(float);
   return L;
 }
 
@@ -184,12 +167,9 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.rows_slot = L.rows_slot;
   p.slot_floats = L.slot_floats;
   p.num_groups = L.num_groups;
-  p.n_xcd = L.n_xcd;
   p.table_mode = L.table_mode;
   p.s_max = L.s_max;
-  p.lg_per_xcd = L.lg_per_xcd;
-  p.seq_per_xcd = L.seq_per_xcd;
-  p.items_per_xcd = L.items_per_xcd;
+  p.item_slots = L.item_slots;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
   p.scale_log2 = scale * kLog2e;
   char* w = static_cast<char*>(ws);
@@ -227,11 +207,13 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
   const size_t dyn = attn_dyn_lds(s, FUSED, p.table_mode);
   const int cus = device_info().cus;
   if (cus <= 0) return kErrHip;
-  const int cap = (cus / L.n_xcd) * occupancy(kern, dyn);
-  int first = L.items_per_xcd < cap ? L.items_per_xcd : cap;
+  const int occ = occupancy(kern, dyn);
+  if (occ < 1) return kErrUnsupported;  // tree rows + item table exceed the LDS
+  const int cap = cus * occ;
+  int first = L.item_slots < cap ? L.item_slots : cap;
   if (first < 1) first = 1;
   p.first_round = first;
-  hipLaunchKernelGGL((attn_kernel<T, D, FUSED>), dim3(unsigned(first * L.n_xcd)), dim3(kThreads),
+  hipLaunchKernelGGL((attn_kernel<T, D, FUSED>), dim3(unsigned(first)), dim3(kAttnThreads),
                      dyn, stream, p);
   return launch_status();
 }
@@ -445,7 +427,6 @@ const char* tree_attn_status_string(ta_status status) {
     case TA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case TA_ERR_BAD_PREFIX: return "prefix length or KV block id out of range (device check)";
     case TA_ERR_TIMEOUT: return "a bounded cross-workgroup wait gave up (device check)";
-    case TA_ERR_PLACEMENT: return "a workgroup ran on an unexpected XCD (device check)";
   }
   return "unknown status";
 }

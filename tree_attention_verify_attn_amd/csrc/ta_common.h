@@ -9,15 +9,16 @@
 namespace ta {
 
 constexpr int kBlock = 64;        // tokens per KV-cache block
-constexpr int kThreads = 256;     // threads per workgroup (4 wave64)
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;     // threads per workgroup of the small kernels (4 wave64)
+constexpr int kAttnThreads = 512; // threads per workgroup of the attention kernel (8 wave64)
+constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kMaxTree = 64;      // one 64-bit mask word per tree node
-constexpr int kMaxBatch = 4096;   // per-workgroup item table lives in LDS
+constexpr int kMaxBatch = 2048;   // per-workgroup item table lives in LDS
 constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
 constexpr unsigned kSpinLimit = 1u << 22;
-constexpr int kMaxXcd = 16;       // XCDs per device the work numbering supports
-constexpr int kCusPerXcd = 32;    // gfx950
+constexpr int kTableBatch = 16;   // batches this large number their items from a prefix table
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 
 // Status codes, identical to ta_status in include/tree_attn.h.
 enum : int {
@@ -29,30 +30,33 @@ enum : int {
   kErrHip = 5,
   kErrBadPrefix = 6,
   kErrTimeout = 7,
-  kErrPlacement = 8,
 };
 
-// First 256 bytes of every workspace.
+constexpr int kCounterStride = 64;  // unsigned words between two counters: one 256-byte line each
+
+// First 768 bytes of every workspace: each field on a cache line of its own,
+// so that the device-scope atomics on one do not queue behind those on another.
 struct WsHeader {
   int error;          // first device-detected error code (0 = none)
+  unsigned pad0[kCounterStride - 1];
   unsigned done;      // workgroups that have left the persistent loop
-  unsigned ticket[kMaxXcd];  // per-XCD next dynamically assigned work item
-  unsigned pad[64 - 2 - kMaxXcd];
+  unsigned pad1[kCounterStride - 1];
+  unsigned ticket;    // next dynamically assigned work item (minus the first round)
+  unsigned pad2[kCounterStride - 1];
 };
-static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+static_assert(sizeof(WsHeader) == 3 * 4 * kCounterStride, "workspace header layout");
 
 // Everything a kernel needs for one call.  Built on the host, passed by value.
 //
 // Work decomposition of the prefix pass.  A group is (sequence b, KV head g,
 // row pass rp); its prefix is cut into chunks of `chunk` tokens, one work item
-// each.  Workgroup i runs on XCD i % n_xcd (the hardware hands workgroups to
-// the XCDs round robin), and every item of a group is given to workgroups of
-// one XCD, so the group's partial results meet in that XCD's L2.  Items of XCD
-// x are numbered li = 0, 1, ...; the first round takes li = i / n_xcd, later
-// ones come from the XCD's ticket counter.
-//   static numbering (table_mode 0): group k = lg * n_xcd + x, li = lg * s_max + s;
-//   table numbering (table_mode 1): sequences b = x, x + n_xcd, ... live on XCD x
-//     and their items are numbered densely from a per-workgroup prefix table.
+// each, and the items of a group have consecutive numbers.  Workgroup i first
+// takes item i, then items from one device-wide ticket counter, in increasing
+// order.  The chunk partials of a group are exchanged through device-coherent
+// (L2-bypassing) accesses, so a group may span XCDs.
+//   static numbering (table_mode 0): li = k * s_max + s for group k;
+//   table numbering (table_mode 1): items numbered densely, sequence by
+//     sequence, from a prefix table every workgroup builds in LDS.
 struct Params {
   const void* q;
   const void* k_cache;
@@ -67,8 +71,8 @@ struct Params {
   void* out;                 // fused: shape dtype;  prefix/suffix: fp32
   float* lse_out;            // may be null in fused mode
   WsHeader* hdr;
-  unsigned* arrive;          // per group arrival counters
-  float* partials;           // [n_xcd * items_per_xcd][slot_floats]
+  unsigned* arrive;          // per group arrival counters, kCounterStride apart
+  float* partials;           // [item slots][slot_floats]
   int batch, hq, hkv, group, head_dim;
   int max_blocks, max_tree, max_prefix, total_nodes, num_blocks;
   int chunk;                 // prefix tokens per work item (multiple of 64)
@@ -76,13 +80,10 @@ struct Params {
   int rows_slot;             // rows reserved per partial slot
   int slot_floats;           // floats per partial slot
   int num_groups;            // batch * hkv * rp_max
-  int n_xcd;                 // XCDs the grid spreads over
-  int table_mode;            // 0 static numbering, 1 per-XCD sequence table
+  int table_mode;            // 0 static numbering, 1 prefix table
   int s_max;                 // chunks per group, upper bound
-  int lg_per_xcd;            // static numbering: groups per XCD
-  int seq_per_xcd;           // table numbering: sequences per XCD (upper bound)
-  int items_per_xcd;         // item slots per XCD
-  int first_round;           // workgroups per XCD in the grid
+  int item_slots;            // num_groups * s_max: bound on item numbers
+  int first_round;           // workgroups in the grid
   int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
   float scale_log2;          // softmax_scale * log2(e)
 };
@@ -91,7 +92,7 @@ struct Params {
 struct WsLayout {
   size_t arrive_off, partial_off, total;
   int rp_max, rows_slot, slot_floats, num_groups, s_max, chunk;
-  int n_xcd, table_mode, lg_per_xcd, seq_per_xcd, items_per_xcd;
+  int table_mode, item_slots;
 };
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -16,20 +16,26 @@
 //   suffix_kernel    tree piece on its own (split path)
 //   merge_kernel     merge of two (o, lse) results (split path)
 //
-// attn_kernel, one work item = sequence b, KV head g, row pass rp, prefix chunk s:
+// attn_kernel, one work item = sequence b, KV head g, row pass rp, prefix chunk s,
+// one workgroup of 8 waves per CU:
 //   * the grouped query rows of (b, g) -- tree node i times the G query heads
-//     sharing KV head g -- form up to four 16-row MFMA tiles, one per wave;
-//   * the chunk's 64-token KV blocks stream HBM -> registers -> LDS (K row-major
-//     with an XOR chunk swizzle, V transposed), PD blocks in flight;
+//     sharing KV head g -- form up to four 16-row MFMA tiles;  wave w takes
+//     row tile w % 4 and key half w / 4 of every 64-key block, with its own
+//     online-softmax state (the two halves are merged once per item);
+//   * the chunk's 64-token KV blocks go HBM -> LDS by direct DMA into a ring of
+//     NS slots (K and V row-major with an XOR chunk swizzle), NS - 1 blocks
+//     ahead of the one being consumed;
 //   * per block each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so a
 //     lane holds one query row and the online softmax needs only the cross-lane
-//     steps l^16, l^32; P^T then feeds O^T += V^T P^T as the MFMA B operand
-//     straight from registers;
-//   * the chunk's partial (unnormalised o, running max, running sum) goes to the
-//     workspace; the items of one group -- all on one XCD, so the exchange stays
-//     in that XCD's L2 -- meet at a counter and split the final combine: each
-//     takes some rows, folds every chunk partial and (fused) the row's tree piece
-//     with their log-sum-exp weights, and writes the output row.
+//     steps l^16, l^32; V^T comes from the transposing LDS read and P^T feeds
+//     O^T += V^T P^T as the MFMA B operand straight from registers;
+//   * fused: the last chunk of a group also stages the group's tree rows and
+//     runs them as one more 64-key block under the ancestor-or-self mask;
+//   * a group with one chunk writes its output rows directly; otherwise each
+//     chunk writes its partial (unnormalised o, running max, running sum) with
+//     device-coherent stores, the chunks meet at a sense-reversing barrier and
+//     split the final combine: each takes some rows, folds every chunk partial
+//     with its log-sum-exp weight and writes the output rows.
 #include <type_traits>
 
 #include "ta_device.h"
@@ -43,10 +49,6 @@ __device__ __forceinline__ unsigned ld_counter(const unsigned* p) {
   return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// XCD this wave runs on (hardware register XCC_ID, bits [3:0]).
-__device__ __forceinline__ int xcc_id() {
-  return int(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)));
-}
 
 // =============================================================== utilities
 __global__ void __launch_bounds__(256) ws_init_kernel(uint4* ws, size_t n16, char* tail,
@@ -90,27 +92,25 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b, bool flag) {
   return make_seq(p, p.tree_offsets[b], p.tree_offsets[b + 1], p.prefix_lens[b], flag);
 }
 
-// Table numbering: cum[j] = items of this XCD's sequences before local sequence
-// j (sequence b = j * n_xcd + x); srp[j] = (chunks, row passes) of sequence j.
-// Returns this XCD's item count.
-__device__ int build_xcd_table(const Params& p, int x, int* cum, int2* srp, int* scratch) {
+// Table numbering: cum[b] = items of the sequences before b; srp[b] packs
+// (chunks << 16) | row passes of sequence b.  Returns the item count.
+__device__ int build_table(const Params& p, int* cum, int* srp, int* scratch) {
   const int tid = threadIdx.x;
-  const int n = p.seq_per_xcd;
-  const int per = cdiv(n, kThreads);
+  const int n = p.batch;
+  const int per = cdiv(n, kAttnThreads);
   const int j0 = min(n, tid * per);
   const int j1 = min(n, j0 + per);
-  const bool flag = blockIdx.x < unsigned(p.n_xcd);
+  const bool flag = blockIdx.x == 0;
   int local = 0;
   for (int j = j0; j < j1; ++j) {
-    const int b = j * p.n_xcd + x;
-    SeqInfo si = b < p.batch ? seq_info(p, b, flag) : SeqInfo{0, 0, 0, 1, 0, 0};
+    const SeqInfo si = seq_info(p, j, flag);
     cum[j + 1] = si.items;
-    srp[j] = make_int2(si.S, si.RP);
+    srp[j] = (si.S << 16) | si.RP;
     local += si.items;
   }
   scratch[tid] = local;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < kAttnThreads; off <<= 1) {
     const int v = tid >= off ? scratch[tid - off] : 0;
     __syncthreads();
     scratch[tid] += v;
@@ -123,7 +123,7 @@ __device__ int build_xcd_table(const Params& p, int x, int* cum, int2* srp, int*
   }
   if (tid == 0) {
     cum[0] = 0;
-    if (blockIdx.x == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
+    if (flag && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
       set_error(p.hdr, kErrBadTree);
   }
   __syncthreads();
@@ -135,18 +135,17 @@ struct Item {
   bool valid;  // false: the static numbering names a group that does not exist
 };
 
-// Decode item li of XCD x into (sequence, KV head, row pass, chunk) without any
+// Decode item li into (sequence, KV head, row pass, chunk) without any
 // global-memory read, so that the item's first loads can all be issued at once.
 // Static numbering may name a chunk or row pass the sequence does not have; the
 // item is then found empty once the sequence's facts arrive.
-__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int2* srp,
-                                            int x, int li) {
+__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int* srp,
+                                            int li) {
   Item it;
   it.valid = true;
   if (p.table_mode == 0) {
-    const int lg = li / p.s_max;
+    const int k = li / p.s_max;
     it.s = li % p.s_max;
-    const int k = lg * p.n_xcd + x;
     it.valid = k < p.num_groups;
     it.grp = it.valid ? k : 0;
     it.rp = it.grp % p.rp_max;
@@ -155,13 +154,13 @@ __device__ __forceinline__ Item decode_item(const Params& p, const int* cum, con
     it.b = bg / p.hkv;
     return it;
   }
-  int lo = 0, hi = p.seq_per_xcd;  // largest j with cum[j] <= li
+  int lo = 0, hi = p.batch;  // largest b with cum[b] <= li
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cum[mid] <= li) lo = mid; else hi = mid;
   }
-  it.b = lo * p.n_xcd + x;
-  const int S = srp[lo].x, RP = srp[lo].y;
+  it.b = lo;
+  const int S = srp[lo] >> 16, RP = srp[lo] & 0xffff;
   const int local = li - cum[lo];
   it.s = local % S;
   const int t = local / S;
@@ -265,25 +264,31 @@ __device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word
 }
 
 // =========================================================== prefix piece
-// LDS of one workgroup.  The two KV ring slots are separate __shared__ objects
+// LDS of one workgroup.  The ring slots are separate __shared__ objects
 // (declared in attn_kernel) so that reads of one slot are not ordered behind
-// the still-running DMA into the other.
+// the still-running DMA into another.
 template <typename T, int D>
 struct Geo {
   static constexpr int ROWB = D * int(sizeof(T));          // bytes per K/V row
   static constexpr int KCH = ROWB / 16;                    // 16-byte chunks per row
   static constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;    // XOR swizzle of chunk index
   static constexpr int BLKB = kBlock * ROWB;               // bytes of one K (or V) block
-  static constexpr int KI = BLKB / (kWaves * 1024);        // DMA instructions per wave per tensor
+  static constexpr int KI = BLKB / (kAttnWaves * 1024);    // DMA instructions per wave per tensor
   static constexpr int QCH = D / 4 * int(sizeof(T)) / 16;  // 16-byte chunks of the Q fragment
   static constexpr int DT = D / 16;                        // 16-wide head-dim tiles of O^T
-  static constexpr int NS = sizeof(T) == 2 ? 2 : 1;        // KV ring slots
+  // ring slots (a K block and a V block each): as many as fit beside the tree
+  // rows and the item table in the 160 KB of LDS of the one workgroup per CU
+  static constexpr int NS = 2 * BLKB <= 16384 ? 4 : (2 * BLKB <= 32768 ? 3 : 1);
+  static_assert(KI >= 1 && BLKB % (kAttnWaves * 1024) == 0, "DMA split");
+  static_assert(NS * 2 * KI < 64, "vmcnt range");
 };
 
 struct SmemMisc {
   uint64_t mask[kMaxTree];
-  int scratch[kThreads];
+  int scratch[kAttnThreads];
   int bcast[4];
+  float half_m[kMaxTree];  // running max / sum of the upper key half, per row
+  float half_l[kMaxTree];
 };
 
 // byte offset of logical 16-byte chunk c of row t in a swizzled row-major tile
@@ -317,7 +322,8 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* a) {
 #endif
 }
 
-// DMA one 64-token K or V block (64 x D, row-major, swizzled) into LDS.
+// DMA one 64-token K or V block (64 x D, row-major, swizzled) into LDS; every
+// wave moves KI kilobytes of it.
 template <typename T, int D>
 __device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char* lds) {
   using Gm = Geo<T, D>;
@@ -339,16 +345,74 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
+// Wait until at most k KV blocks (2 * KI DMA instructions each, the youngest
+// memory operations of the wave) are still in flight; 0 <= k <= NS.
+template <int KI, int NS>
+__device__ __forceinline__ void wait_blocks(int k) {
+  if (NS >= 4 && k >= 4) wait_vm<(NS >= 4 ? 8 * KI : 0)>();
+  else if (NS >= 3 && k >= 3) wait_vm<(NS >= 3 ? 6 * KI : 0)>();
+  else if (k >= 2) wait_vm<4 * KI>();
+  else if (k == 1) wait_vm<2 * KI>();
+  else wait_vm<0>();
+}
 // Barrier that does not drain outstanding loads (the caller waits for what it needs).
 __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_s_waitcnt((0xf) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
   __asm__ __volatile__("s_barrier" ::: "memory");
 }
 
+// Device-coherent accesses to the chunk partials.  The L2 of an XCD is not
+// kept coherent with the others, and the chunks of a group may run on
+// different XCDs, so partials are written and read with the sc1 cache policy
+// (the one the compiler gives agent-scope atomic loads and stores) through a
+// raw buffer descriptor over [base, base + bytes).
+constexpr int kCoherent = 16;  // buffer cache-policy operand selecting sc1
+__device__ __forceinline__ void coherent_store16(float* base, uint32_t bytes, uint32_t off,
+                                                 floatx4 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v),
+                                         __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000),
+                                         int(off), 0, kCoherent);
+#endif
+}
+__device__ __forceinline__ void coherent_store4(float* base, uint32_t bytes, uint32_t off, float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v),
+                                        __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000),
+                                        int(off), 0, kCoherent);
+#endif
+}
+__device__ __forceinline__ float4 coherent_load16(const float* base, uint32_t bytes, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i r = __builtin_amdgcn_raw_buffer_load_b128(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000), int(off), 0,
+      kCoherent);
+  return __builtin_bit_cast(float4, r);
+#else
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+#endif
+}
+__device__ __forceinline__ float coherent_load4(const float* base, uint32_t bytes, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000),
+                 int(off), 0, kCoherent));
+#else
+  return 0.f;
+#endif
+}
+
+// One work item on the 8 waves of a workgroup.  Wave w takes row tile w % 4
+// and key half w / 4 of every 64-key block, with its own online-softmax state;
+// the two halves of a row tile are merged once, at the end of the item.
 template <typename T, int D, bool FUSED>
-__device__ void process_item(const Params& p, unsigned char* slot0, unsigned char* slot1,
-                             unsigned char* tree_lds, SmemMisc& sm, const Item& it,
-                             int slot_index) {
+__device__ __forceinline__ void process_item(const Params& p, unsigned char* ring0,
+                                             unsigned char* ring1, unsigned char* ring2,
+                                             unsigned char* ring3, unsigned char* tree_lds,
+                                             SmemMisc& sm, const Item& it, int slot_index) {
   using Gm = Geo<T, D>;
   constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, SWZ = Gm::SWZ, BLKB = Gm::BLKB, KI = Gm::KI,
                 QCH = Gm::QCH, DT = Gm::DT, NS = Gm::NS;
@@ -357,6 +421,8 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int rt = w & 3;   // row tile
+  const int th = w >> 2;  // key half: keys [32 th, 32 th + 32) of each block
   const int lr = lane & 15;
   const int kq = lane >> 4;
 
@@ -368,9 +434,13 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
     if (lane < p.chunk / kBlock && lb < p.max_blocks)
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
+  // the group's barrier phase (see "meet the other chunks" below), read early
+  unsigned* const counter = p.arrive + size_t(it.grp) * kCounterStride;
+  unsigned* const sense = counter + kCounterStride / 2;
+  unsigned sense0 = 0;
+  if (tid == 0) sense0 = ld_counter(sense);
   const SeqInfo si = seq_info(p, it.b, false);
   if (it.rp >= si.RP || it.s >= si.S) return;  // static numbering: no such item
-
   const int G = p.group;
   const int R = si.T * G;
   const int rlo = it.rp * kRowsPerPass;
@@ -382,19 +452,19 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
   const int S = si.S;
   const size_t head_stride = size_t(kBlock) * D;  // elements per (block, head)
 
-  // ---- tree rows (fused, chunk 0 of the group only: that chunk also attends
+  // ---- tree rows (fused, last chunk of the group only: that chunk also attends
   // to the tree): DMA into LDS, issued before the KV blocks so that waiting
   // for them does not wait for the blocks.  Every staged row past the tree
   // holds a copy of its last node, so all staged rows are finite.
   unsigned char* tk = tree_lds;
   unsigned char* tv = tree_lds + p.tree_lds_half;
   const int tree_rows = p.tree_lds_half / ROWB;  // staged rows (>= tree size)
-  const bool with_tree = FUSED && it.s == 0;
+  const bool with_tree = FUSED && it.s == S - 1;
   int par = -1;
   if (with_tree) {
     const int Tn = si.T;
     const int ninstr = p.tree_lds_half / 1024;
-    for (int m = w; m < ninstr; m += kWaves) {
+    for (int m = w; m < ninstr; m += kAttnWaves) {
       const int u = m * 64 + lane;
       const int t = min(u / KCH, Tn - 1);
       const int pc = u % KCH;
@@ -410,10 +480,10 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
 
   // ---- Q fragment of this wave's row tile: lane (row lr, group kq) holds the
   // contiguous head-dim range [kq*D/4, (kq+1)*D/4) of its row
-  const bool active = w < RT;
+  const bool active = rt < RT;
   uint4 qv[QCH];
   {
-    const int r = 16 * w + lr;
+    const int r = 16 * rt + lr;
     if (active && r < rcount) {
       const int rr = rlo + r;
       const int h = it.g * G + rr % G;
@@ -427,8 +497,8 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
     }
   }
 
-  // ---- KV blocks -> LDS ring
-  auto block_src = [&](int j, int& nvalid) -> size_t {
+  // ---- KV blocks -> LDS ring: block j sits in slot j % NS
+  auto issue = [&](int j, unsigned char* slot, int& nvalid) {
     int id = __shfl(my_id, j);
     const bool ok = id >= 0 && id < p.num_blocks;
     if (!ok) {
@@ -436,30 +506,20 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
       id = 0;
     }
     nvalid = ok ? min(kBlock, ntok - j * kBlock) : 0;
-    return (size_t(id) * p.hkv + it.g) * head_stride;
-  };
-  int nv0 = 0, nv1 = 0;
-  auto issue = [&](int j, unsigned char* slot, int& nv) {
-    const size_t base = block_src(j, nv);
+    const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
     dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot);
     dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB);
   };
-  if (nblk > 0) issue(0, slot0, nv0);
-  if constexpr (NS == 2) {
-    if (nblk > 1) issue(1, slot1, nv1);
-  }
+  int nv0 = 0, nv1 = 0, nv2 = 0, nv3 = 0;
+  if (nblk > 0) issue(0, ring0, nv0);
+  if constexpr (NS > 1) { if (nblk > 1) issue(1, ring1, nv1); }
+  if constexpr (NS > 2) { if (nblk > 2) issue(2, ring2, nv2); }
+  if constexpr (NS > 3) { if (nblk > 3) issue(3, ring3, nv3); }
 
   // ---- tree staging: wait for the tree DMA and parents (older than the
   // blocks), then the tree mask by pointer jumping (as in tree_mask_wave)
   if (with_tree) {
-    if constexpr (NS == 2) {
-      if (nblk > 1) wait_vm<4 * KI>();
-      else if (nblk == 1) wait_vm<2 * KI>();
-      else wait_vm<0>();
-    } else {
-      if (nblk > 0) wait_vm<2 * KI>();
-      else wait_vm<0>();
-    }
+    wait_blocks<KI, NS>(min(nblk, NS));
     if (w == 0) {
       const int Tn = si.T;
       const bool bad_lane = lane < Tn && !(par == -1 || (par >= 0 && par < lane));
@@ -477,8 +537,7 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
         }
       }
       sm.mask[lane] = anc;
-      if (__any(bad_lane) && lane == 0 && it.s == 0 && it.g == 0 && it.rp == 0)
-        set_error(p.hdr, kErrBadTree);
+      if (__any(bad_lane) && lane == 0 && it.g == 0 && it.rp == 0) set_error(p.hdr, kErrBadTree);
     }
   }
 
@@ -491,84 +550,84 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
   // anything there, and 0 * NaN would leak into the PV product)
   auto clear_tail = [&](unsigned char* slot, int nvalid) {
     unsigned char* vb = slot + BLKB;
-    for (int u = tid; u < (kBlock - nvalid) * KCH; u += kThreads) {
+    for (int u = tid; u < (kBlock - nvalid) * KCH; u += kAttnThreads) {
       const int t = nvalid + u / KCH;
       *reinterpret_cast<uint4*>(vb + swz_off<T, D>(t, u % KCH)) = make_uint4(0, 0, 0, 0);
     }
   };
 
-  // One 64-key block: a prefix block (keys < nvalid visible) or, with
-  // kTree, the staged tree rows (key j visible to a row iff bit j of its
-  // node's mask word is set; staged-row reads are clamped to the staging area).
+  // This wave's 32 keys of one 64-key block: a prefix block (keys < nvalid
+  // visible) or, with kTree, the staged tree rows (key j visible to a row iff
+  // bit j of its node's mask word is set; staged-row reads are clamped to the
+  // staging area).  Lane (row lr, group kq) ends up holding scores of keys
+  // 32 th + 16 a + 4 kq + i (a = 0, 1; i = 0..3) of its row.
   auto compute = [&](auto tree_tag, const unsigned char* kb, const unsigned char* vb, int nvalid) {
     constexpr bool kTree = decltype(tree_tag)::value;
     auto krow = [&](int t) { return kTree ? min(t, tree_rows - 1) : t; };
     uint64_t word = 0;
     if constexpr (kTree) {
-      const int r = 16 * w + lr;
+      const int r = 16 * rt + lr;
       word = r < rcount ? sm.mask[(rlo + r) / G] : 0;
     }
     // every LDS read is issued before the MFMAs that consume it
-    uint4 kf[4][QCH];
+    uint4 kf[2][QCH];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int c = 0; c < QCH; ++c)
-        kf[tt][c] = *reinterpret_cast<const uint4*>(kb + swz_off<T, D>(krow(16 * tt + lr), kq * QCH + c));
-    floatx4 sacc[4];
+        kf[a][c] = *reinterpret_cast<const uint4*>(
+            kb + swz_off<T, D>(krow(32 * th + 16 * a + lr), kq * QCH + c));
+    floatx4 sacc[2];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) sacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 2; ++a) sacc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < QCH; ++c)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
+      for (int a = 0; a < 2; ++a) {
         if constexpr (kBf16) {
-          sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kf[tt][c]), __builtin_bit_cast(bf16x8, qv[c]), sacc[tt],
+          sacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kf[a][c]), __builtin_bit_cast(bf16x8, qv[c]), sacc[a],
               0, 0, 0);
         } else {
-          const uint4 kv = kf[tt][c];
+          const uint4 kv = kf[a][c];
           const float ka[4] = {__builtin_bit_cast(float, kv.x), __builtin_bit_cast(float, kv.y),
                                __builtin_bit_cast(float, kv.z), __builtin_bit_cast(float, kv.w)};
           const float qa[4] = {__builtin_bit_cast(float, qv[c].x), __builtin_bit_cast(float, qv[c].y),
                                __builtin_bit_cast(float, qv[c].z), __builtin_bit_cast(float, qv[c].w)};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[tt], 0, 0, 0);
+            sacc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[a], 0, 0, 0);
         }
       }
     // V^T fragments (A operand of O^T += V^T P^T), read while the softmax runs.
     // bf16: the LDS transpose read gives lane (d, group kq) four consecutive
-    // tokens of column d; two of them make the eight k-slots of the MFMA.
-    constexpr int NVF = kBf16 ? 2 * DT : 1;
+    // keys of column d; two of them make the eight k-slots of the MFMA.
+    constexpr int NVF = kBf16 ? DT : 1;
     uint4 vf[NVF];
     if constexpr (kBf16) {
       const int L = lane & 15;
 #pragma unroll
-      for (int f = 0; f < NVF; ++f) {
-        const int kk = f / DT, dt = f % DT;
+      for (int dt = 0; dt < DT; ++dt) {
         uint2 half[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int row = krow(32 * kk + 16 * h + 4 * kq + (L >> 2));
+          const int row = krow(32 * th + 16 * h + 4 * kq + (L >> 2));
           const int cb = 32 * dt + 8 * (L & 3);  // byte column
-          const unsigned char* a = vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15);
-          half[h] = lds_read_tr16(a);
+          half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
         }
-        vf[f] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+        vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
       }
     }
-    // lane (row lr, group kq) holds tokens 16*tt + 4*kq + i of its row
-    float sc[4][4];
+    float sc[2][4];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * tt + 4 * kq + i;
+        const int tok = 32 * th + 16 * a + 4 * kq + i;
         const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
-        sc[tt][i] = vis ? sacc[tt][i] * p.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, sc[tt][i]);
+        sc[a][i] = vis ? sacc[a][i] * p.scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, sc[a][i]);
       }
     bmax = max_over_quads(bmax);
     const float m_new = fmaxf(m_run, bmax);
@@ -581,48 +640,46 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
     m_run = m_new;
-    float pr[4][4];
+    float pr[2][4];
     float rsum = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // the denominator takes the fp32 weight, so the row's lse is exact to
         // fp32 rounding; only the PV operand is rounded to bf16
-        const float e = exp2_fast(sc[tt][i] - m_use);
-        pr[tt][i] = e;
+        const float e = exp2_fast(sc[a][i] - m_use);
+        pr[a][i] = e;
         rsum += e;
       }
     rsum = sum_over_quads(rsum);
     l_run += rsum;
 
     if constexpr (kBf16) {
+      bf16x8 bp;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 bp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bp[i] = static_cast<__bf16>(pr[2 * kk][i]);
-          bp[4 + i] = static_cast<__bf16>(pr[2 * kk + 1][i]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, vf[kk * DT + dt]), bp, oacc[dt], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        bp[i] = static_cast<__bf16>(pr[0][i]);
+        bp[4 + i] = static_cast<__bf16>(pr[1][i]);
       }
-    } else {
-      // fp32: A operand V^T[16dt + lr][16tt + 4kq + i], one element per MFMA
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), bp,
+                                                           oacc[dt], 0, 0, 0);
+    } else {
+      // fp32: A operand V^T[16dt + lr][key], one element per MFMA; k-slot kq of
+      // MFMA (a, i) is key 32 th + 16 a + 4 kq + i
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = krow(16 * tt + 4 * kq + i);
+            const int row = krow(32 * th + 16 * a + 4 * kq + i);
             const int cb = (16 * dt + lr) * 4;
-            const float a = *reinterpret_cast<const float*>(
+            const float av = *reinterpret_cast<const float*>(
                 vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, pr[tt][i], oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pr[a][i], oacc[dt], 0, 0, 0);
           }
     }
   };
@@ -633,15 +690,10 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
     if (active) compute(std::true_type{}, tk, tv, 0);
   }
 
-  // ---- stream the chunk through the ring: block j sits in slot j % NS; the
-  // DMA of block j + NS starts as soon as every wave is done with block j
+  // ---- stream the chunk through the ring; the DMA of block j + NS starts as
+  // soon as every wave is done with block j
   auto step = [&](int j, unsigned char* slot, int& nv) {
-    const bool more = j + 1 < nblk;  // is a later block in flight?
-    if constexpr (NS == 2) {
-      if (more) wait_vm<2 * KI>(); else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_blocks<KI, NS>(min(NS - 1, nblk - 1 - j));
     raw_barrier();
     if (nv < kBlock) {
       clear_tail(slot, nv);
@@ -651,45 +703,109 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
     raw_barrier();
     if (j + NS < nblk) issue(j + NS, slot, nv);
   };
-  if constexpr (NS == 2) {
-    for (int j = 0; j < nblk; j += 2) {
-      step(j, slot0, nv0);
-      if (j + 1 < nblk) step(j + 1, slot1, nv1);
-    }
-  } else {
-    for (int j = 0; j < nblk; ++j) step(j, slot0, nv0);
+  for (int j = 0; j < nblk; j += NS) {
+    step(j, ring0, nv0);
+    if constexpr (NS > 1) { if (j + 1 < nblk) step(j + 1, ring1, nv1); }
+    if constexpr (NS > 2) { if (j + 2 < nblk) step(j + 2, ring2, nv2); }
+    if constexpr (NS > 3) { if (j + 3 < nblk) step(j + 3, ring3, nv3); }
   }
   wait_vm<0>();
   __syncthreads();
 
-  // ---- chunk partial -> workspace (plain stores: read back in this XCD's L2)
-  float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
-  if (active) {
-    const int r = 16 * w + lr;
-    if (r < rcount) {
+  // ---- merge the two key halves of each row tile (lane-major exchange
+  // through ring slot 0, which holds 4 * DT * 64 float4 in every geometry)
+  {
+    floatx4* xo = reinterpret_cast<floatx4*>(ring0);
+    if (th == 1 && active) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<floatx4*>(slotp + r * D + 16 * dt + 4 * kq) = oacc[dt];
+      for (int dt = 0; dt < DT; ++dt) xo[(rt * DT + dt) * 64 + lane] = oacc[dt];
       if (kq == 0) {
-        slotp[p.rows_slot * D + r] = m_run;
-        slotp[p.rows_slot * D + p.rows_slot + r] = l_run;
+        sm.half_m[16 * rt + lr] = m_run;
+        sm.half_l[16 * rt + lr] = l_run;
+      }
+    }
+    __syncthreads();
+    if (th == 0 && active) {
+      const float m1 = sm.half_m[16 * rt + lr];
+      const float l1 = sm.half_l[16 * rt + lr];
+      const float M = fmaxf(m_run, m1);
+      const float mu = M == -INFINITY ? 0.f : M;
+      const float a0 = exp2_fast(m_run - mu);
+      const float a1 = exp2_fast(m1 - mu);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = a0 * oacc[dt] + a1 * xo[(rt * DT + dt) * 64 + lane];
+      l_run = a0 * l_run + a1 * l1;
+      m_run = M;
+    }
+  }
+
+  // ---- a group with a single chunk: normalise and write its rows directly
+  if (S == 1) {
+    if (th == 0 && active) {
+      const int r = 16 * rt + lr;
+      if (r < rcount) {
+        const int rr = rlo + r;
+        const size_t orow = size_t(si.off + rr / G) * p.hq + it.g * G + rr % G;
+        const bool any = m_run != -INFINITY;
+        const float inv = any ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const floatx4 o = oacc[dt] * inv;
+          const size_t e = orow * D + 16 * dt + 4 * kq;
+          if constexpr (FUSED && kBf16) {
+            const uint32_t lo = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + e) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + e) = o;
+          }
+        }
+        if (kq == 0 && p.lse_out)
+          p.lse_out[orow] = any ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+      }
+    }
+    return;
+  }
+
+  // ---- chunk partial -> workspace (device-coherent stores)
+  {
+    float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
+    const uint32_t sbytes = uint32_t(p.slot_floats) * 4u;
+    if (th == 0 && active) {
+      const int r = 16 * rt + lr;
+      if (r < rcount) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          coherent_store16(slotp, sbytes, uint32_t(r * D + 16 * dt + 4 * kq) * 4u, oacc[dt]);
+        if (kq == 0) {
+          coherent_store4(slotp, sbytes, uint32_t(p.rows_slot * D + r) * 4u, m_run);
+          coherent_store4(slotp, sbytes, uint32_t(p.rows_slot * D + p.rows_slot + r) * 4u, l_run);
+        }
       }
     }
   }
 
-  // ---- meet the other chunks of the group (all on this XCD)
-  wait_all_mem();  // this wave's partial stores have reached L2
+  // ---- meet the other chunks of the group: a sense-reversing barrier.  The
+  // arrival counter goes from 0 to S; the chunk that brings it to S resets it
+  // to 0 (ready for the next call) and flips the group's sense word, which the
+  // others poll.  Every chunk's partial stores are complete before its
+  // arrival, so they are all visible once the counter reaches S.
+  wait_all_mem();  // this wave's partial stores are complete
   __syncthreads();
-  if (S > 1) {
+  {
     if (tid == 0) {
-      atomicAdd(p.arrive + it.grp, 1u);
       unsigned spins = 0;
       int timed_out = 0;
-      while (ld_counter(p.arrive + it.grp) < unsigned(S)) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          timed_out = 1;
-          break;
+      if (atomicAdd(counter, 1u) == unsigned(S - 1)) {
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sense, sense0 ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        while (ld_counter(sense) == sense0) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            timed_out = 1;
+            break;
+          }
         }
       }
       if (timed_out) set_error(p.hdr, kErrTimeout);
@@ -703,25 +819,31 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
   // s, s + S, ...  For one row, D/4 lanes (a row slot) cover the head dim, 4
   // elements each; QG row slots split the S chunk partials between them (all
   // loads issued up front), then meet in LDS.  The chunk partials (in the fused
-  // kernel chunk 0's also holds the tree piece) are folded with their
+  // kernel the last chunk's also holds the tree piece) are folded with their
   // log-sum-exp weights.
   // [merge_attentions over disjoint KV chunks: pith.science verdict record,
   // pith_extraction.supporting_citations (Juravsky et al. 2024)]
   {
     constexpr int L4 = D / 4;
-    constexpr int NSLOT = kThreads / L4;
+    constexpr int NSLOT = kAttnThreads / L4;
     constexpr int QMAX = kMaxSplits / NSLOT;
+    // QG row slots per row: enough that QMAX loads per lane cover the S
+    // partials, and no more than lets all of this item's rows (at most
+    // ceil(rcount / S)) go in one pass
     int QG = 1;
-    while (QG < S && QG < NSLOT) QG <<= 1;
+    while (QG * QMAX < S) QG <<= 1;
+    const int rows_here = cdiv(rcount, S);
+    while (2 * QG <= NSLOT && 2 * QG <= S && NSLOT / (2 * QG) >= rows_here) QG <<= 1;
     const int RB = NSLOT / QG;
     const int rs = tid / L4;  // row slot
     const int d4 = tid % L4;
     const int qg = rs % QG;
     const int rb = rs / QG;
-    float* red_m = reinterpret_cast<float*>(slot0);
+    float* red_m = reinterpret_cast<float*>(ring0);
     float* red_l = red_m + NSLOT;
     float* red_o = red_l + NSLOT;                            // [NSLOT][D]
-    const int v0 = slot_index - it.s * p.n_xcd;              // slot of chunk 0
+    const float* g0 = p.partials + size_t(slot_index - it.s) * p.slot_floats;  // chunk 0's slot
+    const uint32_t gbytes = uint32_t(S) * uint32_t(p.slot_floats) * 4u;
     const int moff = p.rows_slot * D;
     const int loff = moff + p.rows_slot;
     for (int k0 = 0; it.s + S * k0 < rcount; k0 += RB) {
@@ -734,10 +856,10 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
       for (int j = 0; j < QMAX; ++j) {
         const int q = qg + QG * j;
         if (valid && q < S) {
-          const float* sl = p.partials + size_t(v0 + q * p.n_xcd) * p.slot_floats;
-          mq[j] = sl[moff + r];
-          lq[j] = sl[loff + r];
-          oq[j] = *reinterpret_cast<const float4*>(sl + r * D + 4 * d4);
+          const uint32_t so = uint32_t(q * p.slot_floats);
+          mq[j] = coherent_load4(g0, gbytes, (so + moff + r) * 4u);
+          lq[j] = coherent_load4(g0, gbytes, (so + loff + r) * 4u);
+          oq[j] = coherent_load16(g0, gbytes, (so + r * D + 4 * d4) * 4u);
         } else {
           mq[j] = -INFINITY;
           lq[j] = 0.f;
@@ -805,52 +927,55 @@ __device__ void process_item(const Params& p, unsigned char* slot0, unsigned cha
 }
 
 template <typename T, int D, bool FUSED>
-__global__ void __launch_bounds__(kThreads, 2) attn_kernel(Params p) {
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   using Gm = Geo<T, D>;
   extern __shared__ __attribute__((aligned(16))) int dyn[];  // tree rows, then the item table
   __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * Gm::BLKB];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[Gm::NS == 2 ? 2 * Gm::BLKB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[Gm::NS > 1 ? 2 * Gm::BLKB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[Gm::NS > 2 ? 2 * Gm::BLKB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[Gm::NS > 3 ? 2 * Gm::BLKB : 16];
   __shared__ SmemMisc sm;
   unsigned char* tree_lds = reinterpret_cast<unsigned char*>(dyn);
-  int* cum = dyn + p.tree_lds_half / 2;  // after 2 * tree_lds_half bytes
-  int2* srp = reinterpret_cast<int2*>(cum + 2 * ((p.seq_per_xcd + 2) / 2));
+  int* cum = dyn + p.tree_lds_half / 2;  // after 2 * tree_lds_half bytes: [batch + 1]
+  int* srp = cum + p.batch + 1;          // [batch]
   const int tid = threadIdx.x;
-  const int x = int(blockIdx.x % unsigned(p.n_xcd));
-  if (p.n_xcd > 1 && tid == 0 && xcc_id() != x) set_error(p.hdr, kErrPlacement);
 
-  int items = p.items_per_xcd;
+  int items = p.item_slots;
   if (p.table_mode) {
-    items = build_xcd_table(p, x, cum, srp, sm.scratch);
+    items = build_table(p, cum, srp, sm.scratch);
   } else if (blockIdx.x == 0) {
     // validate every sequence once (static numbering reads them lazily)
-    for (int b = tid; b < p.batch; b += kThreads) (void)seq_info(p, b, true);
+    for (int b = tid; b < p.batch; b += kAttnThreads) (void)seq_info(p, b, true);
     if (tid == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
       set_error(p.hdr, kErrBadTree);
   }
 
-  int li = int(blockIdx.x / unsigned(p.n_xcd));
+  // items in increasing order: first blockIdx.x, then from the ticket counter.
+  // A workgroup waits only for the other chunks of its own group, whose
+  // numbers are adjacent to its own, and a group has no more chunks than the
+  // grid has workgroups, so every awaited chunk is taken and finished.
+  int li = int(blockIdx.x);
+  const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
-    const Item it = decode_item(p, cum, srp, x, li);
-    if (it.valid) process_item<T, D, FUSED>(p, ring0, ring1, tree_lds, sm, it, li * p.n_xcd + x);
+    const Item it = decode_item(p, cum, srp, li);
+    if (it.valid) process_item<T, D, FUSED>(p, ring0, ring1, ring2, ring3, tree_lds, sm, it, li);
+    if (!tickets) break;
     __syncthreads();
-    if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket[x], 1u));
+    if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket, 1u));
     __syncthreads();
     li = sm.bcast[0];
   }
+  if (!tickets) return;
 
-  // the last workgroup to leave resets the counters for the next call
+  // the last workgroup to leave resets the ticket counter for the next call
+  // (the group barriers reset themselves)
   __syncthreads();
   if (tid == 0) {
     const unsigned n = atomicAdd(&p.hdr->done, 1u);
-    sm.bcast[1] = n == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (sm.bcast[1]) {
-    for (int i = tid; i < p.num_groups; i += kThreads)
-      __hip_atomic_store(p.arrive + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < kMaxXcd)
-      __hip_atomic_store(&p.hdr->ticket[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) __hip_atomic_store(&p.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n == gridDim.x - 1) {
+      __hip_atomic_store(&p.hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
