@@ -8,9 +8,12 @@ already resident in HBM.  Default workload: the Llama-3.1-8B-shaped verify step
 12-node tree).
 
 Timing protocol
-* The 256 MB last-level cache is larger than one batch (33.8 MB), so R
-  independent replicas of the inputs (each its own KV pool, block table, q, tree
-  K/V, >= 1 GiB together) are used in rotation; every step reads HBM.
+* The 256 MB last-level cache is larger than one batch (33.8 MB), so the step
+  rotates over R replicas (>= 1 GiB together) of what differs from one model
+  layer to the next -- the KV pool, q and the tree K/V -- and every step reads
+  them from HBM.  The block table, prefix lengths, parent array and tree
+  offsets are shared by every layer of a verify step, so one copy serves all
+  replicas, as it would in a layer loop.
 * W warm-up steps, then K timed steps queued back to back on one stream.  The
   GPU is first held by a short spin kernel so that the host queues all K steps
   before the first one starts; one pair of HIP events on the launch stream
@@ -40,7 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "tree-verify attention µs/call + achieved HBM GB/s (% of peak), 8k ctx"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_cfg2_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_llama8b_verify_8k_traffic.json")
 
 
 def log(msg: str) -> None:
@@ -145,6 +148,9 @@ def main() -> int:
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=float, default=0.0,
+                    help="instead of the benchmark, run --steps plain device-to-device copies "
+                         "of this many bytes (reference for the HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -166,6 +172,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_bytes > 0:
+        n = int(args.copy_bytes) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "copies": max(1, args.steps)}))
+        return 0
     lib = load()
 
     log(f"building workload cfg{args.config}")
@@ -190,11 +205,13 @@ def main() -> int:
 
     host_arrays = [inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.prefix_lens,
                    inp.k_tree, inp.v_tree, inp.parents, inp.tree_offsets]
-    footprint = sum(a.nbytes for a in host_arrays)
+    per_layer = (0, 1, 2, 5, 6)  # q, k_cache, v_cache, k_tree, v_tree
+    footprint = sum(host_arrays[i].nbytes for i in per_layer)
     R = max(1, math.ceil(args.replica_bytes / footprint))
-    log(f"footprint {footprint / 1e6:.1f} MB -> {R} replicas; split_tokens {split}")
+    log(f"per-layer footprint {footprint / 1e6:.1f} MB -> {R} replicas; split_tokens {split}")
     first = [dev(a) for a in host_arrays]
-    replicas = [first] + [[t.clone() for t in first] for _ in range(R - 1)]
+    replicas = [first] + [[t.clone() if i in per_layer else t for i, t in enumerate(first)]
+                          for _ in range(R - 1)]
     ws = ta.alloc_workspace(shape)
     N, Hq, D = inp.total_tree_nodes, inp.num_q_heads, inp.head_dim
     outs = [torch.empty(N, Hq, D, dtype=first[0].dtype, device="cuda") for _ in range(R)]
@@ -321,7 +338,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": ("attn_kernel<bf16,128,fused> (tree_attn_verify)" if args.entry == "verify"
+            "kernel": (f"attn_kernel<{'bf16' if inp.dtype == 'bf16' else 'f32'},{D},fused> "
+                       "(tree_attn_verify)" if args.entry == "verify"
                        else "split path: mask + prefix + suffix + merge kernels"),
             "mfma_util": round(flops / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
         },
