@@ -122,7 +122,7 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
         oracle.verify(inp)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or calls >= 50:
+        if el >= budget_s:
             break
     per = el / calls
     return {
