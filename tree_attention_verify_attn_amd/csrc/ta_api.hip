@@ -88,9 +88,9 @@ int tree_lds_half(const ta_shape* s, bool fused) {
 }
 
 // Dynamic LDS of the attention kernel: tree rows, then the per-XCD item table.
-size_t attn_dyn_lds(const ta_shape* s, bool fused, int table_mode) {
+size_t attn_dyn_lds(const ta_shape* s, bool fused) {
   size_t bytes = 2 * size_t(tree_lds_half(s, fused));
-  if (table_mode) bytes += size_t(2 * s->batch + 1) * sizeof(int);  // cum[B + 1], srp[B]
+  bytes += size_t(3 * s->batch + 1) * sizeof(int);  // sequence table: cum[B + 1], ot[B], pl[B]
   return 16 * ((bytes + 15) / 16);
 }
 
@@ -98,7 +98,7 @@ size_t attn_dyn_lds(const ta_shape* s, bool fused, int table_mode) {
 int grid_capacity(const ta_shape* s, bool fused) {
   int cus = device_info().cus;
   if (cus <= 0) cus = 256;  // no device: size for a full MI355X, one workgroup per CU
-  const int occ = occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused, s->batch >= kTableBatch));
+  const int occ = occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused));
   return cus * (occ > 0 ? occ : 1);
 }
 
@@ -141,7 +141,6 @@ WsLayout layout_for(const ta_shape* s, int chunk) {
   L.num_groups = s->batch * s->num_kv_heads * L.rp_max;
   L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
   // large batches: dense per-XCD numbering from a prefix table; small: static
-  L.table_mode = s->batch >= kTableBatch ? 1 : 0;
   L.item_slots = L.num_groups * L.s_max;
   L.arrive_off = sizeof(WsHeader);
   L.partial_off = align256(L.arrive_off + sizeof(unsigned) * kCounterStride * size_t(L.num_groups));
@@ -167,7 +166,6 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.rows_slot = L.rows_slot;
   p.slot_floats = L.slot_floats;
   p.num_groups = L.num_groups;
-  p.table_mode = L.table_mode;
   p.s_max = L.s_max;
   p.item_slots = L.item_slots;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
@@ -204,7 +202,7 @@ template <typename T, int D, bool FUSED>
 int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
   const void* kern = attn_ptr<T, D, FUSED>();
   p.tree_lds_half = tree_lds_half(s, FUSED);
-  const size_t dyn = attn_dyn_lds(s, FUSED, p.table_mode);
+  const size_t dyn = attn_dyn_lds(s, FUSED);
   const int cus = device_info().cus;
   if (cus <= 0) return kErrHip;
   const int occ = occupancy(kern, dyn);

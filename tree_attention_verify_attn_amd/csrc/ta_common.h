@@ -17,7 +17,6 @@ constexpr int kMaxBatch = 2048;   // per-workgroup item table lives in LDS
 constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
 constexpr unsigned kSpinLimit = 1u << 22;
-constexpr int kTableBatch = 16;   // batches this large number their items from a prefix table
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 
 // Status codes, identical to ta_status in include/tree_attn.h.
@@ -50,13 +49,12 @@ static_assert(sizeof(WsHeader) == 3 * 4 * kCounterStride, "workspace header layo
 //
 // Work decomposition of the prefix pass.  A group is (sequence b, KV head g,
 // row pass rp); its prefix is cut into chunks of `chunk` tokens, one work item
-// each, and the items of a group have consecutive numbers.  Workgroup i first
-// takes item i, then items from one device-wide ticket counter, in increasing
-// order.  The chunk partials of a group are exchanged through device-coherent
-// (L2-bypassing) accesses, so a group may span XCDs.
-//   static numbering (table_mode 0): li = k * s_max + s for group k;
-//   table numbering (table_mode 1): items numbered densely, sequence by
-//     sequence, from a prefix table every workgroup builds in LDS.
+// each.  Items are numbered densely, sequence by sequence, then KV head, row
+// pass and chunk (chunk fastest), from a table of the sequences every
+// workgroup builds in LDS; the chunks of a group have consecutive numbers.
+// Workgroup i first takes item i, then items from one device-wide ticket
+// counter, in increasing order.  The chunk partials of a group are exchanged
+// through device-coherent (L2-bypassing) accesses, so a group may span XCDs.
 struct Params {
   const void* q;
   const void* k_cache;
@@ -80,7 +78,6 @@ struct Params {
   int rows_slot;             // rows reserved per partial slot
   int slot_floats;           // floats per partial slot
   int num_groups;            // batch * hkv * rp_max
-  int table_mode;            // 0 static numbering, 1 prefix table
   int s_max;                 // chunks per group, upper bound
   int item_slots;            // num_groups * s_max: bound on item numbers
   int first_round;           // workgroups in the grid
@@ -92,7 +89,7 @@ struct Params {
 struct WsLayout {
   size_t arrive_off, partial_off, total;
   int rp_max, rows_slot, slot_floats, num_groups, s_max, chunk;
-  int table_mode, item_slots;
+  int item_slots;
 };
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -92,9 +92,12 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b, bool flag) {
   return make_seq(p, p.tree_offsets[b], p.tree_offsets[b + 1], p.prefix_lens[b], flag);
 }
 
-// Table numbering: cum[b] = items of the sequences before b; srp[b] packs
-// (chunks << 16) | row passes of sequence b.  Returns the item count.
-__device__ int build_table(const Params& p, int* cum, int* srp, int* scratch) {
+// Per-workgroup sequence table in LDS, built once per launch: cum[b] = items
+// of the sequences before b, ot[b] = tree offset | tree size << 24, pl[b] =
+// prefix length, all validated (the first workgroup flags bad data).  With it
+// an item's facts need no global read.  Returns the item count.
+constexpr int kTreeSizeShift = 24;  // tree offsets < 2^24 (<= 2048 trees of <= 64 nodes)
+__device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* scratch) {
   const int tid = threadIdx.x;
   const int n = p.batch;
   const int per = cdiv(n, kAttnThreads);
@@ -105,7 +108,8 @@ __device__ int build_table(const Params& p, int* cum, int* srp, int* scratch) {
   for (int j = j0; j < j1; ++j) {
     const SeqInfo si = seq_info(p, j, flag);
     cum[j + 1] = si.items;
-    srp[j] = (si.S << 16) | si.RP;
+    ot[j] = int(unsigned(si.off) | (unsigned(si.T) << kTreeSizeShift));
+    pl[j] = si.P;
     local += si.items;
   }
   scratch[tid] = local;
@@ -132,40 +136,34 @@ __device__ int build_table(const Params& p, int* cum, int* srp, int* scratch) {
 
 struct Item {
   int b, g, rp, s, grp;
-  bool valid;  // false: the static numbering names a group that does not exist
+  SeqInfo si;
 };
 
-// Decode item li into (sequence, KV head, row pass, chunk) without any
-// global-memory read, so that the item's first loads can all be issued at once.
-// Static numbering may name a chunk or row pass the sequence does not have; the
-// item is then found empty once the sequence's facts arrive.
-__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int* srp,
-                                            int li) {
+// Decode item li into (sequence, KV head, row pass, chunk) and the sequence's
+// facts from the LDS table, without any global-memory read.  Items are
+// numbered sequence by sequence, then KV head, row pass and chunk (chunk
+// fastest), so the chunks of a group have consecutive numbers.
+__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int* ot,
+                                            const int* pl, int li) {
   Item it;
-  it.valid = true;
-  if (p.table_mode == 0) {
-    const int k = li / p.s_max;
-    it.s = li % p.s_max;
-    it.valid = k < p.num_groups;
-    it.grp = it.valid ? k : 0;
-    it.rp = it.grp % p.rp_max;
-    const int bg = it.grp / p.rp_max;
-    it.g = bg % p.hkv;
-    it.b = bg / p.hkv;
-    return it;
-  }
   int lo = 0, hi = p.batch;  // largest b with cum[b] <= li
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cum[mid] <= li) lo = mid; else hi = mid;
   }
   it.b = lo;
-  const int S = srp[lo] >> 16, RP = srp[lo] & 0xffff;
+  const unsigned o = unsigned(ot[lo]);
+  it.si.off = int(o & ((1u << kTreeSizeShift) - 1u));
+  it.si.T = int(o >> kTreeSizeShift);
+  it.si.P = pl[lo];
+  it.si.S = it.si.P > 0 ? cdiv(it.si.P, p.chunk) : 1;
+  it.si.RP = cdiv(it.si.T * p.group, kRowsPerPass);
+  it.si.items = cum[lo + 1] - cum[lo];
   const int local = li - cum[lo];
-  it.s = local % S;
-  const int t = local / S;
-  it.rp = t % RP;
-  it.g = t / RP;
+  it.s = local % it.si.S;
+  const int t = local / it.si.S;
+  it.rp = t % it.si.RP;
+  it.g = t / it.si.RP;
   it.grp = (it.b * p.hkv + it.g) * p.rp_max + it.rp;
   return it;
 }
@@ -264,9 +262,8 @@ __device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word
 }
 
 // =========================================================== prefix piece
-// LDS of one workgroup.  The ring slots are separate __shared__ objects
-// (declared in attn_kernel) so that reads of one slot are not ordered behind
-// the still-running DMA into another.
+// LDS of one workgroup: a ring of NS KV slots (declared in attn_kernel), the
+// tree rows and the sequence table (dynamic), and SmemMisc.
 template <typename T, int D>
 struct Geo {
   static constexpr int ROWB = D * int(sizeof(T));          // bytes per K/V row
@@ -298,12 +295,27 @@ __device__ __forceinline__ int swz_off(int t, int c) {
   return t * Gm::ROWB + ((c ^ (t & Gm::SWZ)) << 4);
 }
 
-// One 16-byte global -> LDS transfer per lane: the lane's 16 bytes from g land
-// at lds_base + 16 * lane (lds_base is wave-uniform).  The address-space cast
-// exists only for the device target, so the host pass sees an empty body.
+// Direct global -> LDS transfers (16 bytes per lane, landing at lds_base + 16 *
+// lane; lds_base wave-uniform) are written as inline assembly on purpose.  The
+// compiler, when it sees them as LDS writes, cannot tell which LDS object an
+// in-flight transfer targets and makes every later LDS read wait for all
+// outstanding transfers, including the prefetched KV blocks, which would
+// serialise the ring.  Here every wait is explicit: a slot is read only after
+// a vmcnt wait that covers its transfers and a barrier.  M0 carries the LDS
+// address and is set in the same statement.  The address-space cast exists
+// only for the device target, so the host pass sees empty bodies.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+#else
+  return uint32_t(reinterpret_cast<uintptr_t>(p));
+#endif
+}
+// lane's 16 bytes from its own global address g
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
 #endif
 }
 
@@ -322,21 +334,53 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* a) {
 #endif
 }
 
-// DMA one 64-token K or V block (64 x D, row-major, swizzled) into LDS; every
-// wave moves KI kilobytes of it.
+// Source byte offsets, within one 64-token K or V tile, of the 16-byte chunks
+// this lane moves: instruction i of wave w fills LDS chunks (w KI + i) 64 +
+// lane, i.e. row t, physical chunk pc, which holds logical chunk pc ^ (t & SWZ).
 template <typename T, int D>
-__device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char* lds) {
+__device__ __forceinline__ void dma_offsets(uint32_t* off) {
   using Gm = Geo<T, D>;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < Gm::KI; ++i) {
-    const int u = (w * Gm::KI + i) * 64 + lane;  // LDS chunk this lane fills
+    const int u = (w * Gm::KI + i) * 64 + lane;
     const int t = u / Gm::KCH;
     const int pc = u % Gm::KCH;
-    const int c = pc ^ (t & Gm::SWZ);
-    lds_dma16(g + t * Gm::ROWB + c * 16, lds + (w * Gm::KI + i) * 1024);
+    off[i] = uint32_t(t * Gm::ROWB + ((pc ^ (t & Gm::SWZ)) << 4));
   }
+}
+
+// lane's 16 bytes from [tile, tile + bytes) at byte offset voff, through a raw
+// buffer descriptor (tile wave-uniform, in scalar registers; the only vector
+// operand is the 32-bit offset; an offset past `bytes` reads zeros)
+__device__ __forceinline__ void lds_dma16_tile(const void* tile, uint32_t bytes, uint32_t voff,
+                                               void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t a = reinterpret_cast<uint64_t>(tile);
+  const u32x4 desc = {uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a))),
+                      uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu)),
+                      uint32_t(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
+  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
+               "s"(desc)
+               : "memory");
+#endif
+}
+
+// DMA one 64-token K or V tile (64 x D, row-major, swizzled) into LDS; every
+// wave moves KI kilobytes of it.  `g` is wave-uniform.  The per-lane offsets
+// stay in the same registers for the whole item, so no instruction writes a
+// register that a transfer still in flight names (the compiler would make it
+// wait for every outstanding transfer first).
+template <typename T, int D>
+__device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char* lds,
+                                          const uint32_t* off) {
+  using Gm = Geo<T, D>;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < Gm::KI; ++i) lds_dma16_tile(g, Gm::BLKB, off[i], lds + (w * Gm::KI + i) * 1024);
 }
 
 // Wait until at most n of this wave's vector-memory operations are outstanding.
@@ -409,10 +453,10 @@ __device__ __forceinline__ float coherent_load4(const float* base, uint32_t byte
 // and key half w / 4 of every 64-key block, with its own online-softmax state;
 // the two halves of a row tile are merged once, at the end of the item.
 template <typename T, int D, bool FUSED>
-__device__ __forceinline__ void process_item(const Params& p, unsigned char* ring0,
-                                             unsigned char* ring1, unsigned char* ring2,
-                                             unsigned char* ring3, unsigned char* tree_lds,
-                                             SmemMisc& sm, const Item& it, int slot_index) {
+__device__ __forceinline__ void process_item(const Params& p, unsigned char* ring,
+                                             unsigned char* tree_lds,
+                                             SmemMisc& sm, const Item& it, int slot_index,
+                                             bool solo_combine) {
   using Gm = Geo<T, D>;
   constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, SWZ = Gm::SWZ, BLKB = Gm::BLKB, KI = Gm::KI,
                 QCH = Gm::QCH, DT = Gm::DT, NS = Gm::NS;
@@ -421,26 +465,10 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int rt = w & 3;   // row tile
-  const int th = w >> 2;  // key half: keys [32 th, 32 th + 32) of each block
   const int lr = lane & 15;
   const int kq = lane >> 4;
 
-  // block ids of the chunk (lane j: block j) and the sequence's facts, read in
-  // one round trip; ids past the sequence's prefix are never used
-  int my_id = -1;
-  {
-    const int lb = it.s * (p.chunk / kBlock) + lane;
-    if (lane < p.chunk / kBlock && lb < p.max_blocks)
-      my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
-  }
-  // the group's barrier phase (see "meet the other chunks" below), read early
-  unsigned* const counter = p.arrive + size_t(it.grp) * kCounterStride;
-  unsigned* const sense = counter + kCounterStride / 2;
-  unsigned sense0 = 0;
-  if (tid == 0) sense0 = ld_counter(sense);
-  const SeqInfo si = seq_info(p, it.b, false);
-  if (it.rp >= si.RP || it.s >= si.S) return;  // static numbering: no such item
+  const SeqInfo si = it.si;
   const int G = p.group;
   const int R = si.T * G;
   const int rlo = it.rp * kRowsPerPass;
@@ -451,36 +479,26 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   const int nblk = cdiv(ntok, kBlock);
   const int S = si.S;
   const size_t head_stride = size_t(kBlock) * D;  // elements per (block, head)
+  const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
+  // Wave roles: row tile rt and key part kp of every 64-key block.  With at
+  // most two row tiles a block is cut into four 16-key parts (so that even a
+  // single row tile keeps all four SIMDs busy), else into two 32-key halves.
+  const int RTW = RT <= 1 ? 1 : (RT <= 2 ? 2 : 4);
+  const int KP = RT <= 2 ? 4 : 2;
+  const int rt = w % RTW;
+  const int kp = w / RTW;
+  const bool active = rt < RT && kp < KP;
 
-  // ---- tree rows (fused, last chunk of the group only: that chunk also attends
-  // to the tree): DMA into LDS, issued before the KV blocks so that waiting
-  // for them does not wait for the blocks.  Every staged row past the tree
-  // holds a copy of its last node, so all staged rows are finite.
-  unsigned char* tk = tree_lds;
-  unsigned char* tv = tree_lds + p.tree_lds_half;
-  const int tree_rows = p.tree_lds_half / ROWB;  // staged rows (>= tree size)
-  const bool with_tree = FUSED && it.s == S - 1;
-  int par = -1;
-  if (with_tree) {
-    const int Tn = si.T;
-    const int ninstr = p.tree_lds_half / 1024;
-    for (int m = w; m < ninstr; m += kAttnWaves) {
-      const int u = m * 64 + lane;
-      const int t = min(u / KCH, Tn - 1);
-      const int pc = u % KCH;
-      const int c = pc ^ ((u / KCH) & SWZ);
-      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
-      const unsigned char* gk = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff);
-      const unsigned char* gv = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff);
-      lds_dma16(gk + c * 16, tk + m * 1024);
-      lds_dma16(gv + c * 16, tv + m * 1024);
-    }
-    if (w == 0) par = p.parents[si.off + min(lane, Tn - 1)];
-  }
-
-  // ---- Q fragment of this wave's row tile: lane (row lr, group kq) holds the
-  // contiguous head-dim range [kq*D/4, (kq+1)*D/4) of its row
-  const bool active = rt < RT;
+  // ---- one round trip for every global value the item needs in registers:
+  // the group's barrier phase, the Q fragment of this wave's row tile (lane
+  // (row lr, group kq) holds the head-dim range [kq*D/4, (kq+1)*D/4) of its
+  // row), the tree's parent array and, last, the chunk's block ids (lane j:
+  // block j).  All of it is complete before the first LDS transfer is issued,
+  // so no later wait for these values can hold up the transfers.
+  unsigned* const counter = p.arrive + size_t(it.grp) * kCounterStride;
+  unsigned* const sense = counter + kCounterStride / 2;
+  unsigned sense0 = 0;
+  if (tid == 0) sense0 = ld_counter(sense);
   uint4 qv[QCH];
   {
     const int r = 16 * rt + lr;
@@ -496,28 +514,62 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int c = 0; c < QCH; ++c) qv[c] = make_uint4(0, 0, 0, 0);
     }
   }
+  int par = -1;
+  if (with_tree && w == 0) par = p.parents[si.off + min(lane, si.T - 1)];
+  int my_id = -1;
+  {
+    const int lb = it.s * (p.chunk / kBlock) + lane;
+    if (lane < p.chunk / kBlock && lb < p.max_blocks)
+      my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
+  }
+  wait_vm<0>();
 
-  // ---- KV blocks -> LDS ring: block j sits in slot j % NS
-  auto issue = [&](int j, unsigned char* slot, int& nvalid) {
-    int id = __shfl(my_id, j);
-    const bool ok = id >= 0 && id < p.num_blocks;
-    if (!ok) {
+  // ---- tree rows (fused, last chunk only): DMA into LDS, issued before the KV
+  // blocks so that waiting for them does not wait for the blocks.  Every
+  // staged row past the tree holds a copy of its last node, so all staged rows
+  // are finite.
+  unsigned char* tk = tree_lds;
+  unsigned char* tv = tree_lds + p.tree_lds_half;
+  const int tree_rows = p.tree_lds_half / ROWB;  // staged rows (>= tree size)
+  if (with_tree) {
+    const int Tn = si.T;
+    const int ninstr = p.tree_lds_half / 1024;
+    for (int m = w; m < ninstr; m += kAttnWaves) {
+      const int u = m * 64 + lane;
+      const int t = min(u / KCH, Tn - 1);
+      const int pc = u % KCH;
+      const int c = pc ^ ((u / KCH) & SWZ);
+      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+      const unsigned char* gk = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff);
+      const unsigned char* gv = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff);
+      lds_dma16(gk + c * 16, tk + m * 1024);
+      lds_dma16(gv + c * 16, tv + m * 1024);
+    }
+  }
+
+  // ---- KV blocks -> LDS ring: block j sits in slot j % NS.  A block id out
+  // of range is flagged, its DMA reads block 0 instead and the block counts
+  // as empty (bit j of `bad`).
+  constexpr int SLOTB = 2 * BLKB;  // K tile, then V tile
+  uint32_t doff[KI];
+  dma_offsets<T, D>(doff);
+  uint64_t bad = 0;
+  auto issue = [&](int j) {
+    int id = __builtin_amdgcn_readfirstlane(__shfl(my_id, j));  // wave-uniform
+    if (!(id >= 0 && id < p.num_blocks)) {
       if (tid == 0) set_error(p.hdr, kErrBadPrefix);
+      bad |= uint64_t(1) << j;
       id = 0;
     }
-    nvalid = ok ? min(kBlock, ntok - j * kBlock) : 0;
+    unsigned char* slot = ring + (j % NS) * SLOTB;
     const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
-    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot);
-    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB);
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot, doff);
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB, doff);
   };
-  int nv0 = 0, nv1 = 0, nv2 = 0, nv3 = 0;
-  if (nblk > 0) issue(0, ring0, nv0);
-  if constexpr (NS > 1) { if (nblk > 1) issue(1, ring1, nv1); }
-  if constexpr (NS > 2) { if (nblk > 2) issue(2, ring2, nv2); }
-  if constexpr (NS > 3) { if (nblk > 3) issue(3, ring3, nv3); }
+  for (int j = 0; j < NS && j < nblk; ++j) issue(j);
 
-  // ---- tree staging: wait for the tree DMA and parents (older than the
-  // blocks), then the tree mask by pointer jumping (as in tree_mask_wave)
+  // ---- tree staging: wait for the tree DMA (older than the blocks), then the
+  // tree mask by pointer jumping (as in tree_mask_wave)
   if (with_tree) {
     wait_blocks<KI, NS>(min(nblk, NS));
     if (w == 0) {
@@ -556,13 +608,17 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     }
   };
 
-  // This wave's 32 keys of one 64-key block: a prefix block (keys < nvalid
-  // visible) or, with kTree, the staged tree rows (key j visible to a row iff
-  // bit j of its node's mask word is set; staged-row reads are clamped to the
-  // staging area).  Lane (row lr, group kq) ends up holding scores of keys
-  // 32 th + 16 a + 4 kq + i (a = 0, 1; i = 0..3) of its row.
-  auto compute = [&](auto tree_tag, const unsigned char* kb, const unsigned char* vb, int nvalid) {
+  // This wave's KS keys (key part kp) of one 64-key block: a prefix block
+  // (keys < nvalid visible) or, with kTree, the staged tree rows (key j
+  // visible to a row iff bit j of its node's mask word is set; staged-row
+  // reads are clamped to the staging area).  Lane (row lr, group kq) ends up
+  // holding scores of keys kp KS + 16 a + 4 kq + i (a < KS / 16, i < 4).
+  auto compute = [&](auto tree_tag, auto ks_tag, const unsigned char* kb, const unsigned char* vb,
+                     int nvalid) {
     constexpr bool kTree = decltype(tree_tag)::value;
+    constexpr int KS = decltype(ks_tag)::value;  // 16 or 32 keys
+    constexpr int NA = KS / 16;                  // 16-key tiles
+    const int kbase = kp * KS;
     auto krow = [&](int t) { return kTree ? min(t, tree_rows - 1) : t; };
     uint64_t word = 0;
     if constexpr (kTree) {
@@ -570,20 +626,20 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       word = r < rcount ? sm.mask[(rlo + r) / G] : 0;
     }
     // every LDS read is issued before the MFMAs that consume it
-    uint4 kf[2][QCH];
+    uint4 kf[NA][QCH];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int c = 0; c < QCH; ++c)
         kf[a][c] = *reinterpret_cast<const uint4*>(
-            kb + swz_off<T, D>(krow(32 * th + 16 * a + lr), kq * QCH + c));
-    floatx4 sacc[2];
+            kb + swz_off<T, D>(krow(kbase + 16 * a + lr), kq * QCH + c));
+    floatx4 sacc[NA];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) sacc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < NA; ++a) sacc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < QCH; ++c)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < NA; ++a) {
         if constexpr (kBf16) {
           sacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, kf[a][c]), __builtin_bit_cast(bf16x8, qv[c]), sacc[a],
@@ -600,31 +656,33 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
         }
       }
     // V^T fragments (A operand of O^T += V^T P^T), read while the softmax runs.
-    // bf16: the LDS transpose read gives lane (d, group kq) four consecutive
-    // keys of column d; two of them make the eight k-slots of the MFMA.
+    // The transposing LDS read gives lane (d, group kq) four consecutive keys
+    // of column d: one read makes the four k-slots of a 16-key MFMA, two make
+    // the eight of a 32-key one.
     constexpr int NVF = kBf16 ? DT : 1;
     uint4 vf[NVF];
     if constexpr (kBf16) {
       const int L = lane & 15;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        uint2 half[2];
+        uint2 half[NA];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = krow(32 * th + 16 * h + 4 * kq + (L >> 2));
+        for (int h = 0; h < NA; ++h) {
+          const int row = krow(kbase + 16 * h + 4 * kq + (L >> 2));
           const int cb = 32 * dt + 8 * (L & 3);  // byte column
           half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
         }
-        vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+        if constexpr (NA == 2) vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+        else vf[dt] = make_uint4(half[0].x, half[0].y, 0u, 0u);
       }
     }
-    float sc[2][4];
+    float sc[NA][4];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 32 * th + 16 * a + 4 * kq + i;
+        const int tok = kbase + 16 * a + 4 * kq + i;
         const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
         sc[a][i] = vis ? sacc[a][i] * p.scale_log2 : -INFINITY;
         bmax = fmaxf(bmax, sc[a][i]);
@@ -640,10 +698,10 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
     m_run = m_new;
-    float pr[2][4];
+    float pr[NA][4];
     float rsum = 0.f;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         // the denominator takes the fp32 weight, so the row's lse is exact to
@@ -656,26 +714,39 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     l_run += rsum;
 
     if constexpr (kBf16) {
-      bf16x8 bp;
+      if constexpr (NA == 2) {
+        bf16x8 bp;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bp[i] = static_cast<__bf16>(pr[0][i]);
-        bp[4 + i] = static_cast<__bf16>(pr[1][i]);
+        for (int i = 0; i < 4; ++i) {
+          bp[i] = static_cast<__bf16>(pr[0][i]);
+          bp[4 + i] = static_cast<__bf16>(pr[1][i]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), bp,
+                                                             oacc[dt], 0, 0, 0);
+      } else {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        v4i16 bp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bp[i] = short(f32_to_bf16(pr[0][i]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint2 va = make_uint2(vf[dt].x, vf[dt].y);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, va), bp,
+                                                               oacc[dt], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), bp,
-                                                           oacc[dt], 0, 0, 0);
     } else {
       // fp32: A operand V^T[16dt + lr][key], one element per MFMA; k-slot kq of
-      // MFMA (a, i) is key 32 th + 16 a + 4 kq + i
+      // MFMA (a, i) is key kbase + 16 a + 4 kq + i
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = krow(32 * th + 16 * a + 4 * kq + i);
+            const int row = krow(kbase + 16 * a + 4 * kq + i);
             const int cb = (16 * dt + lr) * 4;
             const float av = *reinterpret_cast<const float*>(
                 vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
@@ -683,65 +754,72 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
           }
     }
   };
+  // the wave's part of one block, with the part size of this item
+  auto run_block = [&](auto tree_tag, const unsigned char* kb, const unsigned char* vb, int nvalid) {
+    if (KP == 4) compute(tree_tag, std::integral_constant<int, 16>{}, kb, vb, nvalid);
+    else compute(tree_tag, std::integral_constant<int, 32>{}, kb, vb, nvalid);
+  };
 
   // ---- the tree piece, while the first KV blocks are still in flight
   if (with_tree) {
     raw_barrier();  // staged rows of every wave and the mask words are in LDS
-    if (active) compute(std::true_type{}, tk, tv, 0);
+    if (active) run_block(std::true_type{}, tk, tv, 0);
   }
 
   // ---- stream the chunk through the ring; the DMA of block j + NS starts as
   // soon as every wave is done with block j
-  auto step = [&](int j, unsigned char* slot, int& nv) {
+  for (int j = 0; j < nblk; ++j) {
+    unsigned char* slot = ring + (j % NS) * SLOTB;
+    const int nv = ((bad >> j) & 1) ? 0 : min(kBlock, ntok - j * kBlock);
     wait_blocks<KI, NS>(min(NS - 1, nblk - 1 - j));
     raw_barrier();
     if (nv < kBlock) {
       clear_tail(slot, nv);
       raw_barrier();
     }
-    if (active) compute(std::false_type{}, slot, slot + BLKB, nv);
+    if (active) run_block(std::false_type{}, slot, slot + BLKB, nv);
     raw_barrier();
-    if (j + NS < nblk) issue(j + NS, slot, nv);
-  };
-  for (int j = 0; j < nblk; j += NS) {
-    step(j, ring0, nv0);
-    if constexpr (NS > 1) { if (j + 1 < nblk) step(j + 1, ring1, nv1); }
-    if constexpr (NS > 2) { if (j + 2 < nblk) step(j + 2, ring2, nv2); }
-    if constexpr (NS > 3) { if (j + 3 < nblk) step(j + 3, ring3, nv3); }
+    if (j + NS < nblk) issue(j + NS);
   }
   wait_vm<0>();
   __syncthreads();
 
-  // ---- merge the two key halves of each row tile (lane-major exchange
-  // through ring slot 0, which holds 4 * DT * 64 float4 in every geometry)
+  // ---- merge the key parts of each row tile, pairwise (part kp + half into
+  // part kp), in one or two rounds; the lane-major exchange goes through ring
+  // slot 0, which holds the 4 * DT * 64 float4 of one round in every geometry
   {
-    floatx4* xo = reinterpret_cast<floatx4*>(ring0);
-    if (th == 1 && active) {
+    floatx4* xo = reinterpret_cast<floatx4*>(ring);
+    for (int half = KP / 2; half >= 1; half >>= 1) {
+      if (active && kp >= half && kp < 2 * half) {
+        const int e = (kp - half) * RTW + rt;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) xo[(rt * DT + dt) * 64 + lane] = oacc[dt];
-      if (kq == 0) {
-        sm.half_m[16 * rt + lr] = m_run;
-        sm.half_l[16 * rt + lr] = l_run;
+        for (int dt = 0; dt < DT; ++dt) xo[(e * DT + dt) * 64 + lane] = oacc[dt];
+        if (kq == 0) {
+          sm.half_m[16 * e + lr] = m_run;
+          sm.half_l[16 * e + lr] = l_run;
+        }
       }
-    }
-    __syncthreads();
-    if (th == 0 && active) {
-      const float m1 = sm.half_m[16 * rt + lr];
-      const float l1 = sm.half_l[16 * rt + lr];
-      const float M = fmaxf(m_run, m1);
-      const float mu = M == -INFINITY ? 0.f : M;
-      const float a0 = exp2_fast(m_run - mu);
-      const float a1 = exp2_fast(m1 - mu);
+      __syncthreads();
+      if (active && kp < half) {
+        const int e = kp * RTW + rt;
+        const float m1 = sm.half_m[16 * e + lr];
+        const float l1 = sm.half_l[16 * e + lr];
+        const float M = fmaxf(m_run, m1);
+        const float mu = M == -INFINITY ? 0.f : M;
+        const float a0 = exp2_fast(m_run - mu);
+        const float a1 = exp2_fast(m1 - mu);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] = a0 * oacc[dt] + a1 * xo[(rt * DT + dt) * 64 + lane];
-      l_run = a0 * l_run + a1 * l1;
-      m_run = M;
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = a0 * oacc[dt] + a1 * xo[(e * DT + dt) * 64 + lane];
+        l_run = a0 * l_run + a1 * l1;
+        m_run = M;
+      }
+      __syncthreads();
     }
   }
 
   // ---- a group with a single chunk: normalise and write its rows directly
   if (S == 1) {
-    if (th == 0 && active) {
+    if (kp == 0 && active) {
       const int r = 16 * rt + lr;
       if (r < rcount) {
         const int rr = rlo + r;
@@ -771,7 +849,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   {
     float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
     const uint32_t sbytes = uint32_t(p.slot_floats) * 4u;
-    if (th == 0 && active) {
+    if (kp == 0 && active) {
       const int r = 16 * rt + lr;
       if (r < rcount) {
 #pragma unroll
@@ -785,14 +863,30 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     }
   }
 
-  // ---- meet the other chunks of the group: a sense-reversing barrier.  The
-  // arrival counter goes from 0 to S; the chunk that brings it to S resets it
-  // to 0 (ready for the next call) and flips the group's sense word, which the
-  // others poll.  Every chunk's partial stores are complete before its
-  // arrival, so they are all visible once the counter reaches S.
+  // ---- meet the other chunks of the group.  The arrival counter goes from 0
+  // to S, and the chunk that brings it to S resets it to 0 (ready for the next
+  // call).  Every chunk's partial stores are complete before its arrival, so
+  // they are all visible to whoever sees the counter reach S.
+  //   solo_combine (items are handed out over several rounds, so the chunks
+  //   of a group may run far apart in time): nobody waits; the chunk that
+  //   arrives last combines every row of the group.
+  //   otherwise (all chunks run at once): a sense-reversing barrier -- the
+  //   last arrival flips the group's sense word, the others poll it -- and
+  //   the S chunks then split the rows of the combine.
   wait_all_mem();  // this wave's partial stores are complete
   __syncthreads();
-  {
+  int r0 = it.s, rstride = S;  // rows this workgroup combines: r0, r0 + rstride, ...
+  if (solo_combine) {
+    if (tid == 0) {
+      const bool last = atomicAdd(counter, 1u) == unsigned(S - 1);
+      if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.bcast[2] = last;
+    }
+    __syncthreads();
+    if (!sm.bcast[2]) return;
+    r0 = 0;
+    rstride = 1;
+  } else {
     if (tid == 0) {
       unsigned spins = 0;
       int timed_out = 0;
@@ -815,8 +909,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     if (sm.bcast[2]) return;
   }
 
-  // ---- combine.  The S items of the group share its rows: item s takes rows
-  // s, s + S, ...  For one row, D/4 lanes (a row slot) cover the head dim, 4
+  // ---- combine.  This workgroup takes rows r0, r0 + rstride, ... of the
+  // group (rows s, s + S, ... when the S chunks split the combine; every row
+  // when it combines alone).  For one row, D/4 lanes (a row slot) cover the head dim, 4
   // elements each; QG row slots split the S chunk partials between them (all
   // loads issued up front), then meet in LDS.  The chunk partials (in the fused
   // kernel the last chunk's also holds the tree piece) are folded with their
@@ -828,26 +923,26 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     constexpr int NSLOT = kAttnThreads / L4;
     constexpr int QMAX = kMaxSplits / NSLOT;
     // QG row slots per row: enough that QMAX loads per lane cover the S
-    // partials, and no more than lets all of this item's rows (at most
-    // ceil(rcount / S)) go in one pass
+    // partials, and no more than lets all of this workgroup's rows go in one
+    // pass
     int QG = 1;
     while (QG * QMAX < S) QG <<= 1;
-    const int rows_here = cdiv(rcount, S);
+    const int rows_here = cdiv(rcount - r0, rstride);
     while (2 * QG <= NSLOT && 2 * QG <= S && NSLOT / (2 * QG) >= rows_here) QG <<= 1;
     const int RB = NSLOT / QG;
     const int rs = tid / L4;  // row slot
     const int d4 = tid % L4;
     const int qg = rs % QG;
     const int rb = rs / QG;
-    float* red_m = reinterpret_cast<float*>(ring0);
+    float* red_m = reinterpret_cast<float*>(ring);
     float* red_l = red_m + NSLOT;
     float* red_o = red_l + NSLOT;                            // [NSLOT][D]
     const float* g0 = p.partials + size_t(slot_index - it.s) * p.slot_floats;  // chunk 0's slot
     const uint32_t gbytes = uint32_t(S) * uint32_t(p.slot_floats) * 4u;
     const int moff = p.rows_slot * D;
     const int loff = moff + p.rows_slot;
-    for (int k0 = 0; it.s + S * k0 < rcount; k0 += RB) {
-      const int r = it.s + S * (k0 + rb);
+    for (int k0 = 0; r0 + rstride * k0 < rcount; k0 += RB) {
+      const int r = r0 + rstride * (k0 + rb);
       const bool valid = r < rcount;
       const int rr = rlo + r;
       float mq[QMAX], lq[QMAX];
@@ -930,25 +1025,15 @@ template <typename T, int D, bool FUSED>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   using Gm = Geo<T, D>;
   extern __shared__ __attribute__((aligned(16))) int dyn[];  // tree rows, then the item table
-  __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * Gm::BLKB];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[Gm::NS > 1 ? 2 * Gm::BLKB : 16];
-  __shared__ __attribute__((aligned(16))) unsigned char ring2[Gm::NS > 2 ? 2 * Gm::BLKB : 16];
-  __shared__ __attribute__((aligned(16))) unsigned char ring3[Gm::NS > 3 ? 2 * Gm::BLKB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[Gm::NS * 2 * Gm::BLKB];
   __shared__ SmemMisc sm;
   unsigned char* tree_lds = reinterpret_cast<unsigned char*>(dyn);
   int* cum = dyn + p.tree_lds_half / 2;  // after 2 * tree_lds_half bytes: [batch + 1]
-  int* srp = cum + p.batch + 1;          // [batch]
+  int* ot = cum + p.batch + 1;           // [batch]
+  int* pl = ot + p.batch;                // [batch]
   const int tid = threadIdx.x;
 
-  int items = p.item_slots;
-  if (p.table_mode) {
-    items = build_table(p, cum, srp, sm.scratch);
-  } else if (blockIdx.x == 0) {
-    // validate every sequence once (static numbering reads them lazily)
-    for (int b = tid; b < p.batch; b += kAttnThreads) (void)seq_info(p, b, true);
-    if (tid == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
-      set_error(p.hdr, kErrBadTree);
-  }
+  const int items = build_table(p, cum, ot, pl, sm.scratch);
 
   // items in increasing order: first blockIdx.x, then from the ticket counter.
   // A workgroup waits only for the other chunks of its own group, whose
@@ -957,8 +1042,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int li = int(blockIdx.x);
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
-    const Item it = decode_item(p, cum, srp, li);
-    if (it.valid) process_item<T, D, FUSED>(p, ring0, ring1, ring2, ring3, tree_lds, sm, it, li);
+    const Item it = decode_item(p, cum, ot, pl, li);
+    process_item<T, D, FUSED>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
     if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket, 1u));
