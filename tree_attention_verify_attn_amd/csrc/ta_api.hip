@@ -88,9 +88,31 @@ int tree_lds_half(const ta_shape* s, bool fused) {
 }
 
 // Dynamic LDS of the attention kernel: tree rows, then the per-XCD item table.
-size_t attn_dyn_lds(const ta_shape* s, bool fused) {
+// bytes of one KV ring slot (a 64-token K tile and V tile)
+size_t ring_slot_bytes(const ta_shape* s) {
+  return size_t(2) * kBlock * s->head_dim * (s->dtype == TA_DTYPE_BF16 ? 2 : 4);
+}
+
+// LDS of the attention kernel besides the ring: tree rows, sequence table
+// (cum[B + 1], ot[B], pl[B]) and the static SmemMisc
+size_t attn_fixed_lds(const ta_shape* s, bool fused) {
   size_t bytes = 2 * size_t(tree_lds_half(s, fused));
-  bytes += size_t(3 * s->batch + 1) * sizeof(int);  // sequence table: cum[B + 1], ot[B], pl[B]
+  bytes += size_t(3 * s->batch + 1) * sizeof(int);
+  return 16 * ((bytes + 15) / 16) + sizeof(SmemMisc) + 256;
+}
+
+// Ring slots that fit in one CU's LDS (0 if not even one does).
+int ring_slots(const ta_shape* s, bool fused) {
+  const size_t fixed = attn_fixed_lds(s, fused);
+  if (fixed >= size_t(kLdsBytes)) return 0;
+  size_t n = (size_t(kLdsBytes) - fixed) / ring_slot_bytes(s);
+  return int(n < size_t(kMaxRingSlots) ? n : size_t(kMaxRingSlots));
+}
+
+size_t attn_dyn_lds(const ta_shape* s, bool fused) {
+  size_t bytes = size_t(ring_slots(s, fused)) * ring_slot_bytes(s);
+  bytes += 2 * size_t(tree_lds_half(s, fused));
+  bytes += size_t(3 * s->batch + 1) * sizeof(int);
   return 16 * ((bytes + 15) / 16);
 }
 
@@ -202,7 +224,11 @@ template <typename T, int D, bool FUSED>
 int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
   const void* kern = attn_ptr<T, D, FUSED>();
   p.tree_lds_half = tree_lds_half(s, FUSED);
+  p.ns = ring_slots(s, FUSED);
+  if (p.ns < 1) return kErrUnsupported;  // tree rows + sequence table leave no room for the ring
   const size_t dyn = attn_dyn_lds(s, FUSED);
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn)) != hipSuccess)
+    return kErrHip;
   const int cus = device_info().cus;
   if (cus <= 0) return kErrHip;
   const int occ = occupancy(kern, dyn);

@@ -18,6 +18,7 @@ constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
+constexpr int kMaxRingSlots = 3;       // KV blocks the attention kernel keeps in LDS
 
 // Status codes, identical to ta_status in include/tree_attn.h.
 enum : int {
@@ -82,6 +83,7 @@ struct Params {
   int item_slots;            // num_groups * s_max: bound on item numbers
   int first_round;           // workgroups in the grid
   int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
+  int ns;                    // KV ring slots in LDS, 1..kMaxRingSlots
   float scale_log2;          // softmax_scale * log2(e)
 };
 

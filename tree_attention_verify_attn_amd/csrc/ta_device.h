@@ -54,15 +54,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA output row).
+// Exchange with lane l ^ 16 and with lane l ^ 32 on the VALU
+// (v_permlane16_swap / v_permlane32_swap), no LDS round trip.  Called with
+// the same value in both operands, the pair returned holds, in every lane,
+// the lane's own value and its partner's (in an order that depends on the
+// lane), so a symmetric reduction of the pair is the reduction over the two.
 __device__ __forceinline__ float max_over_quads(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, unsigned(a[0])), __builtin_bit_cast(float, unsigned(a[1])));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(b[0])), __builtin_bit_cast(float, unsigned(b[1])));
 }
 __device__ __forceinline__ float sum_over_quads(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  v = __builtin_bit_cast(float, unsigned(a[0])) + __builtin_bit_cast(float, unsigned(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, unsigned(b[0])) + __builtin_bit_cast(float, unsigned(b[1]));
 }
 // Reductions over a 32-lane half-wave.
 __device__ __forceinline__ float max_over_32(float v) {

@@ -273,11 +273,13 @@ struct Geo {
   static constexpr int KI = BLKB / (kAttnWaves * 1024);    // DMA instructions per wave per tensor
   static constexpr int QCH = D / 4 * int(sizeof(T)) / 16;  // 16-byte chunks of the Q fragment
   static constexpr int DT = D / 16;                        // 16-wide head-dim tiles of O^T
-  // ring slots (a K block and a V block each): as many as fit beside the tree
-  // rows and the item table in the 160 KB of LDS of the one workgroup per CU
-  static constexpr int NS = 2 * BLKB <= 16384 ? 4 : (2 * BLKB <= 32768 ? 3 : 1);
+  // ring slots (a K block and a V block each): the host gives each launch as
+  // many as fit beside the tree rows and the sequence table in the 160 KB of
+  // LDS of the one workgroup per CU, at most NSMAX
+  static constexpr int NSMAX = kMaxRingSlots;
+  static constexpr int SLOTB = 2 * BLKB;
   static_assert(KI >= 1 && BLKB % (kAttnWaves * 1024) == 0, "DMA split");
-  static_assert(NS * 2 * KI < 64, "vmcnt range");
+  static_assert(NSMAX * 2 * KI < 64, "vmcnt range");
 };
 
 struct SmemMisc {
@@ -459,7 +461,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
                                              bool solo_combine) {
   using Gm = Geo<T, D>;
   constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, SWZ = Gm::SWZ, BLKB = Gm::BLKB, KI = Gm::KI,
-                QCH = Gm::QCH, DT = Gm::DT, NS = Gm::NS;
+                QCH = Gm::QCH, DT = Gm::DT, NSMAX = Gm::NSMAX;
+  const int NS = p.ns;  // ring slots of this launch, 1..NSMAX
   constexpr bool kBf16 = sizeof(T) == 2;
 
   const int tid = threadIdx.x;
@@ -550,7 +553,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // ---- KV blocks -> LDS ring: block j sits in slot j % NS.  A block id out
   // of range is flagged, its DMA reads block 0 instead and the block counts
   // as empty (bit j of `bad`).
-  constexpr int SLOTB = 2 * BLKB;  // K tile, then V tile
+  constexpr int SLOTB = Gm::SLOTB;  // K tile, then V tile
   uint32_t doff[KI];
   dma_offsets<T, D>(doff);
   uint64_t bad = 0;
@@ -571,7 +574,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // ---- tree staging: wait for the tree DMA (older than the blocks), then the
   // tree mask by pointer jumping (as in tree_mask_wave)
   if (with_tree) {
-    wait_blocks<KI, NS>(min(nblk, NS));
+    wait_blocks<KI, NSMAX>(min(nblk, NS));
     if (w == 0) {
       const int Tn = si.T;
       const bool bad_lane = lane < Tn && !(par == -1 || (par >= 0 && par < lane));
@@ -625,7 +628,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       const int r = 16 * rt + lr;
       word = r < rcount ? sm.mask[(rlo + r) / G] : 0;
     }
-    // every LDS read is issued before the MFMAs that consume it
+    // every LDS read of the block is issued before the first MFMA
     uint4 kf[NA][QCH];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -633,6 +636,30 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int c = 0; c < QCH; ++c)
         kf[a][c] = *reinterpret_cast<const uint4*>(
             kb + swz_off<T, D>(krow(kbase + 16 * a + lr), kq * QCH + c));
+    // V^T fragments (A operand of O^T += V^T P^T), read together with K so
+    // that their latency overlaps the QK product and the softmax.
+    // The transposing LDS read gives lane (d, group kq) four consecutive keys
+    // of column d: one read makes the four k-slots of a 16-key MFMA, two make
+    // the eight of a 32-key one.
+    constexpr int NVF = kBf16 ? DT : 1;
+    uint4 vf[NVF];
+    if constexpr (kBf16) {
+      const int L = lane & 15;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 half[NA];
+#pragma unroll
+        for (int h = 0; h < NA; ++h) {
+          const int row = krow(kbase + 16 * h + 4 * kq + (L >> 2));
+          const int cb = 32 * dt + 8 * (L & 3);  // byte column
+          half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
+        }
+        if constexpr (NA == 2) vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
+        else vf[dt] = make_uint4(half[0].x, half[0].y, 0u, 0u);
+      }
+    }
+    // keep every read above this point: one LDS round trip per block
+    __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[NA];
 #pragma unroll
     for (int a = 0; a < NA; ++a) sacc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -655,27 +682,6 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
             sacc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[a], 0, 0, 0);
         }
       }
-    // V^T fragments (A operand of O^T += V^T P^T), read while the softmax runs.
-    // The transposing LDS read gives lane (d, group kq) four consecutive keys
-    // of column d: one read makes the four k-slots of a 16-key MFMA, two make
-    // the eight of a 32-key one.
-    constexpr int NVF = kBf16 ? DT : 1;
-    uint4 vf[NVF];
-    if constexpr (kBf16) {
-      const int L = lane & 15;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        uint2 half[NA];
-#pragma unroll
-        for (int h = 0; h < NA; ++h) {
-          const int row = krow(kbase + 16 * h + 4 * kq + (L >> 2));
-          const int cb = 32 * dt + 8 * (L & 3);  // byte column
-          half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
-        }
-        if constexpr (NA == 2) vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
-        else vf[dt] = make_uint4(half[0].x, half[0].y, 0u, 0u);
-      }
-    }
     float sc[NA][4];
     float bmax = -INFINITY;
 #pragma unroll
@@ -771,7 +777,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   for (int j = 0; j < nblk; ++j) {
     unsigned char* slot = ring + (j % NS) * SLOTB;
     const int nv = ((bad >> j) & 1) ? 0 : min(kBlock, ntok - j * kBlock);
-    wait_blocks<KI, NS>(min(NS - 1, nblk - 1 - j));
+    wait_blocks<KI, NSMAX>(min(NS - 1, nblk - 1 - j));
     raw_barrier();
     if (nv < kBlock) {
       clear_tail(slot, nv);
@@ -1024,11 +1030,12 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
 template <typename T, int D, bool FUSED>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   using Gm = Geo<T, D>;
-  extern __shared__ __attribute__((aligned(16))) int dyn[];  // tree rows, then the item table
-  __shared__ __attribute__((aligned(16))) unsigned char ring[Gm::NS * 2 * Gm::BLKB];
+  // dynamic LDS: the KV ring (ns slots), the tree rows (K then V), the table
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
   __shared__ SmemMisc sm;
-  unsigned char* tree_lds = reinterpret_cast<unsigned char*>(dyn);
-  int* cum = dyn + p.tree_lds_half / 2;  // after 2 * tree_lds_half bytes: [batch + 1]
+  unsigned char* ring = reinterpret_cast<unsigned char*>(dyn);
+  unsigned char* tree_lds = ring + size_t(p.ns) * Gm::SLOTB;
+  int* cum = reinterpret_cast<int*>(tree_lds + 2 * p.tree_lds_half);  // [batch + 1]
   int* ot = cum + p.batch + 1;           // [batch]
   int* pl = ot + p.batch;                // [batch]
   const int tid = threadIdx.x;
