@@ -93,11 +93,18 @@ size_t ring_slot_bytes(const ta_shape* s) {
   return size_t(2) * kBlock * s->head_dim * (s->dtype == TA_DTYPE_BF16 ? 2 : 4);
 }
 
+// ints of the sequence table: cum[B + 1], ot[B], pl[B], perm[pow2 >= B]
+size_t table_ints(const ta_shape* s) {
+  size_t np = 1;
+  while (np < size_t(s->batch)) np <<= 1;
+  return size_t(3 * s->batch + 1) + np;
+}
+
 // LDS of the attention kernel besides the ring: tree rows, sequence table
-// (cum[B + 1], ot[B], pl[B]) and the static SmemMisc
+// and the static SmemMisc
 size_t attn_fixed_lds(const ta_shape* s, bool fused) {
   size_t bytes = 2 * size_t(tree_lds_half(s, fused));
-  bytes += size_t(3 * s->batch + 1) * sizeof(int);
+  bytes += table_ints(s) * sizeof(int);
   return 16 * ((bytes + 15) / 16) + sizeof(SmemMisc) + 256;
 }
 
@@ -112,7 +119,7 @@ int ring_slots(const ta_shape* s, bool fused) {
 size_t attn_dyn_lds(const ta_shape* s, bool fused) {
   size_t bytes = size_t(ring_slots(s, fused)) * ring_slot_bytes(s);
   bytes += 2 * size_t(tree_lds_half(s, fused));
-  bytes += size_t(3 * s->batch + 1) * sizeof(int);
+  bytes += table_ints(s) * sizeof(int);
   return 16 * ((bytes + 15) / 16);
 }
 

@@ -92,46 +92,143 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b, bool flag) {
   return make_seq(p, p.tree_offsets[b], p.tree_offsets[b + 1], p.prefix_lens[b], flag);
 }
 
-// Per-workgroup sequence table in LDS, built once per launch: cum[b] = items
-// of the sequences before b, ot[b] = tree offset | tree size << 24, pl[b] =
-// prefix length, all validated (the first workgroup flags bad data).  With it
-// an item's facts need no global read.  Returns the item count.
+// Per-workgroup sequence table in LDS, built once per launch.  Sequences are
+// placed in processing order: when the items need more than one round of
+// workgroups, longest prefix first (sorted by the class floor(log2 P),
+// ties by index, the same order in every workgroup), so that the last items
+// handed out are the shortest; otherwise in index order.  For position k:
+// perm[k] = the sequence (low 11 bits), cum[k] = items before it, ot[k] =
+// tree offset | tree size << 24, pl[k] = prefix length, all validated (the
+// first workgroup flags bad data).  With it an item's facts need no global
+// read.  Returns the item count.
 constexpr int kTreeSizeShift = 24;  // tree offsets < 2^24 (<= 2048 trees of <= 64 nodes)
-__device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* scratch) {
+constexpr int kSeqBits = 11;        // sequence index bits in a sort key (batch <= 2048)
+// Exclusive prefix sum of v over the workgroup's threads (in thread order) and
+// the total: a scan inside each wave, then the wave totals through LDS (one
+// barrier).  Every thread must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int x = 0; x < kAttnWaves; ++x) {
+    const int t = scratch[x];
+    before += x < w ? t : 0;
+    total += t;
+  }
+  __syncthreads();  // scratch may be reused right after
+  return before + inc - v;
+}
+
+__device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* perm, int* scratch) {
   const int tid = threadIdx.x;
   const int n = p.batch;
   const int per = cdiv(n, kAttnThreads);
   const int j0 = min(n, tid * per);
   const int j1 = min(n, j0 + per);
   const bool flag = blockIdx.x == 0;
+  // facts in index order, the item prefix in index order
+  constexpr int kPerMax = kMaxBatch / kAttnThreads;
+  int items_q[kPerMax];
   int local = 0;
-  for (int j = j0; j < j1; ++j) {
-    const SeqInfo si = seq_info(p, j, flag);
-    cum[j + 1] = si.items;
-    ot[j] = int(unsigned(si.off) | (unsigned(si.T) << kTreeSizeShift));
-    pl[j] = si.P;
-    local += si.items;
+#pragma unroll
+  for (int q = 0; q < kPerMax; ++q) {
+    const int j = j0 + q;
+    items_q[q] = 0;
+    if (j < j1) {
+      const SeqInfo si = seq_info(p, j, flag);
+      ot[j] = int(unsigned(si.off) | (unsigned(si.T) << kTreeSizeShift));
+      pl[j] = si.P;
+      perm[j] = j;
+      items_q[q] = si.items;
+      local += si.items;
+    }
   }
-  scratch[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kAttnThreads; off <<= 1) {
-    const int v = tid >= off ? scratch[tid - off] : 0;
+  int total = 0;
+  int run = block_exclusive_scan(local, scratch, total);
+  const bool sort = n > 1 && total > p.first_round;
+  if (!sort) {
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q)
+      if (j0 + q < j1) {
+        cum[j0 + q] = run;
+        run += items_q[q];
+      }
+  } else {
+    // processing order: keys (length class, index) ascending = longest first
+    const int np = [&] { int v = 1; while (v < n) v <<= 1; return v; }();
+    for (int i = tid; i < np; i += kAttnThreads) {
+      int key = 0x7fffffff;  // padding sorts last
+      if (i < n) {
+        const int P = pl[i];
+        const int cls = 31 - __clz(P > 1 ? P : 1);  // 0..15
+        key = ((15 - cls) << kSeqBits) | i;
+      }
+      perm[i] = key;
+    }
     __syncthreads();
-    scratch[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? scratch[tid - 1] : 0;
-  for (int j = j0; j < j1; ++j) {
-    run += cum[j + 1];
-    cum[j + 1] = run;
+    for (int k = 2; k <= np; k <<= 1)
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < np; i += kAttnThreads) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const int a = perm[i], b = perm[ixj];
+            if ((a > b) == ((i & k) == 0)) {
+              perm[i] = b;
+              perm[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    // facts and item prefix in processing order (gathered through registers,
+    // written back in place after the scan's barrier)
+    int g_ot[kPerMax], g_pl[kPerMax];
+    local = 0;
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) {
+      const int k = j0 + q;
+      items_q[q] = 0;
+      g_ot[q] = 0;
+      g_pl[q] = 0;
+      if (k < j1) {
+        const int j = perm[k] & ((1 << kSeqBits) - 1);
+        g_ot[q] = ot[j];
+        g_pl[q] = pl[j];
+        const int P = g_pl[q];
+        const int T = int(unsigned(g_ot[q]) >> kTreeSizeShift);
+        items_q[q] = p.hkv * cdiv(T * p.group, kRowsPerPass) * (P > 0 ? cdiv(P, p.chunk) : 1);
+        local += items_q[q];
+      }
+    }
+    run = block_exclusive_scan(local, scratch, total);
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) {
+      const int k = j0 + q;
+      if (k < j1) {
+        ot[k] = g_ot[q];
+        pl[k] = g_pl[q];
+        cum[k] = run;
+        run += items_q[q];
+      }
+    }
   }
   if (tid == 0) {
-    cum[0] = 0;
+    cum[n] = total;
     if (flag && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
       set_error(p.hdr, kErrBadTree);
   }
   __syncthreads();
-  return cum[n];
+  return total;
 }
 
 struct Item {
@@ -144,14 +241,14 @@ struct Item {
 // numbered sequence by sequence, then KV head, row pass and chunk (chunk
 // fastest), so the chunks of a group have consecutive numbers.
 __device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int* ot,
-                                            const int* pl, int li) {
+                                            const int* pl, const int* perm, int li) {
   Item it;
   int lo = 0, hi = p.batch;  // largest b with cum[b] <= li
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cum[mid] <= li) lo = mid; else hi = mid;
   }
-  it.b = lo;
+  it.b = perm[lo] & ((1 << kSeqBits) - 1);
   const unsigned o = unsigned(ot[lo]);
   it.si.off = int(o & ((1u << kTreeSizeShift) - 1u));
   it.si.T = int(o >> kTreeSizeShift);
@@ -451,6 +548,10 @@ __device__ __forceinline__ float coherent_load4(const float* base, uint32_t byte
 #endif
 }
 
+// Slack (log2 units) by which a block's max may exceed the running reference
+// max before the reference moves; weights stay <= 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.f;
+
 // One work item on the 8 waves of a workgroup.  Wave w takes row tile w % 4
 // and key half w / 4 of every 64-key block, with its own online-softmax state;
 // the two halves of a row tile are merged once, at the end of the item.
@@ -682,28 +783,41 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
             sacc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], qa[e], sacc[a], 0, 0, 0);
         }
       }
-    float sc[NA][4];
-    float bmax = -INFINITY;
+    // Online softmax in base 2.  Scores stay unscaled until the exponent; the
+    // running reference max m_run is in scaled units.  Only a partial block or
+    // the tree block needs the per-key mask.
+    const float c = p.scale_log2;
+    const bool masked = kTree || nvalid < kBlock;
+    float sr[NA][4];
+    float rmax = -INFINITY;
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = kbase + 16 * a + 4 * kq + i;
-        const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
-        sc[a][i] = vis ? sacc[a][i] * p.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, sc[a][i]);
+        float v = sacc[a][i];
+        if (masked) {
+          const int tok = kbase + 16 * a + 4 * kq + i;
+          const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
+          v = vis ? v : -INFINITY;
+        }
+        sr[a][i] = v;
+        rmax = fmaxf(rmax, v);
       }
-    bmax = max_over_quads(bmax);
-    const float m_new = fmaxf(m_run, bmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    // rescale the running output only when some row's max rose (alpha == 1 else)
-    if (__any(m_new > m_run)) {
-      const float alpha = exp2_fast(m_run - m_use);
+    rmax = max_over_quads(rmax);
+    const float m_cand = rmax * c;  // -inf stays -inf (c > 0)
+    // Move the reference only when this block's max exceeds it by more than
+    // kRescaleSlack: the weights then stay <= 2^kRescaleSlack, and the costly
+    // rescale of the running output is rare after the first block.  The
+    // result does not depend on the reference (o / l and lse = m + log2 l).
+    if (__any(m_cand > m_run + kRescaleSlack)) {
+      const float m_new = m_cand > m_run + kRescaleSlack ? m_cand : m_run;
+      const float alpha = m_new == m_run ? 1.f : exp2_fast(m_run - m_new);  // 0 from -inf
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float pr[NA][4];
     float rsum = 0.f;
 #pragma unroll
@@ -712,7 +826,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int i = 0; i < 4; ++i) {
         // the denominator takes the fp32 weight, so the row's lse is exact to
         // fp32 rounding; only the PV operand is rounded to bf16
-        const float e = exp2_fast(sc[a][i] - m_use);
+        const float e = exp2_fast(fmaf(sr[a][i], c, -m_use));
         pr[a][i] = e;
         rsum += e;
       }
@@ -1038,9 +1152,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int* cum = reinterpret_cast<int*>(tree_lds + 2 * p.tree_lds_half);  // [batch + 1]
   int* ot = cum + p.batch + 1;           // [batch]
   int* pl = ot + p.batch;                // [batch]
+  int* perm = pl + p.batch;              // [pow2 >= batch]
   const int tid = threadIdx.x;
 
-  const int items = build_table(p, cum, ot, pl, sm.scratch);
+  const int items = build_table(p, cum, ot, pl, perm, sm.scratch);
 
   // items in increasing order: first blockIdx.x, then from the ticket counter.
   // A workgroup waits only for the other chunks of its own group, whose
@@ -1049,7 +1164,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int li = int(blockIdx.x);
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
-    const Item it = decode_item(p, cum, ot, pl, li);
+    const Item it = decode_item(p, cum, ot, pl, perm, li);
     process_item<T, D, FUSED>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
