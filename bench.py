@@ -43,7 +43,11 @@ sys.path.insert(0, ROOT)
 METRIC = "tree-verify attention µs/call + achieved HBM GB/s (% of peak), 8k ctx"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_llama8b_verify_8k_traffic.json")
+# counter-measured HBM traffic of the fused kernel, per workload (see profiles/)
+TRAFFIC_FILES = {
+    2: os.path.join(ROOT, "profiles", "attn_kernel_llama8b_verify_8k_traffic.json"),
+    5: os.path.join(ROOT, "profiles", "attn_kernel_ragged_b256_traffic.json"),
+}
 
 
 def log(msg: str) -> None:
@@ -96,8 +100,11 @@ def kernel_source_hash() -> str:
 def measured_traffic(config_index: int, split: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel sources and the same workload; else None."""
+    path = TRAFFIC_FILES.get(config_index)
+    if path is None:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
