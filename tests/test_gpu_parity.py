@@ -288,3 +288,38 @@ def test_verify_device_errors_flagged():
     out, lse = run_verify(d)
     assert ta.get_error(d.workspace) == 0
     _check_verify(inp, out, lse, "after errors")
+
+
+@pytest.mark.gpu
+def test_verify_device_errors_flagged_single_sequence():
+    """One-sequence launches read the prefix length inside each item; bad data
+    is still flagged and never read out of bounds."""
+    import tree_attention_verify_attn_amd as ta
+    inp = small_inputs(91, dtype="bf16", B=1, Hq=8, Hkv=2, D=128, prefix_lens=(700,),
+                       trees=[[-1, 0, 0, 1, 2]])
+    d = to_device(inp, max_prefix_len=704, split_tokens=128)
+    d.prefix_lens[0] = 705
+    say("single-sequence device error: prefix beyond bound")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 6
+    d.prefix_lens[0] = int(inp.prefix_lens[0])
+    good = int(inp.block_table[0, 3])
+    d.block_table[0, 3] = inp.num_blocks + 1
+    say("single-sequence device error: block id out of range")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 6
+    d.block_table[0, 3] = good
+    d.parents[1] = 7
+    say("single-sequence device error: bad parent")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 3
+    d.parents[1] = int(inp.parents[1])
+    d.tree_offsets[1] = int(inp.tree_offsets[1]) - 1
+    say("single-sequence device error: bad tree offsets")
+    run_verify(d)
+    assert ta.get_error(d.workspace) == 3
+    d.tree_offsets[1] = int(inp.tree_offsets[1])
+    say("single-sequence device error: clean call after errors")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, "single after errors")

@@ -197,6 +197,9 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.num_groups = L.num_groups;
   p.s_max = L.s_max;
   p.item_slots = L.item_slots;
+  // one sequence whose tree is every row of q: no sequence table needed
+  p.single = (s->batch == 1 && s->total_tree_nodes >= 1 && s->total_tree_nodes <= s->max_tree_nodes) ? 1 : 0;
+  p.single_items = p.single ? s->num_kv_heads * cdiv(s->total_tree_nodes * p.group, kRowsPerPass) * L.s_max : 0;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
   p.scale_log2 = scale * kLog2e;
   char* w = static_cast<char*>(ws);

@@ -81,6 +81,8 @@ struct Params {
   int num_groups;            // batch * hkv * rp_max
   int s_max;                 // chunks per group, upper bound
   int item_slots;            // num_groups * s_max: bound on item numbers
+  int single;                // 1: one sequence, items numbered without a table
+  int single_items;          // item count of a one-sequence launch
   int first_round;           // workgroups in the grid
   int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
   int ns;                    // KV ring slots in LDS, 1..kMaxRingSlots

@@ -265,6 +265,28 @@ __device__ __forceinline__ Item decode_item(const Params& p, const int* cum, con
   return it;
 }
 
+// Decode item li of a one-sequence launch without a table: the tree is the
+// whole of q's rows (offset 0, N nodes, both known to the host), the chunk
+// count is the bound s_max from max_prefix_len, and the prefix length is
+// read with the item's other values (si.P = -1 until then); a chunk past the
+// actual prefix turns out empty.
+__device__ __forceinline__ Item decode_single(const Params& p, int li) {
+  Item it;
+  it.b = 0;
+  it.si.off = 0;
+  it.si.T = p.total_nodes;
+  it.si.P = -1;
+  it.si.S = p.s_max;
+  it.si.RP = cdiv(it.si.T * p.group, kRowsPerPass);
+  it.si.items = p.hkv * it.si.RP * it.si.S;
+  it.s = li % it.si.S;
+  const int t = li / it.si.S;
+  it.rp = t % it.si.RP;
+  it.g = t / it.si.RP;
+  it.grp = it.g * p.rp_max + it.rp;
+  return it;
+}
+
 // ====================================================== suffix (tree) piece
 // D/4 consecutive lanes (one "row slot") compute the tree piece of one grouped
 // query row: the keys are the tree nodes whose bit is set in `word`.  Lane d4
@@ -572,18 +594,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   const int lr = lane & 15;
   const int kq = lane >> 4;
 
-  const SeqInfo si = it.si;
+  SeqInfo si = it.si;
+  const bool need_p = si.P < 0;  // one-sequence numbering: the prefix length is read below
   const int G = p.group;
   const int R = si.T * G;
   const int rlo = it.rp * kRowsPerPass;
   const int rcount = min(kRowsPerPass, R - rlo);
   const int RT = cdiv(rcount, 16);
-  const int t0 = it.s * p.chunk;
-  const int ntok = max(0, min(si.P, t0 + p.chunk) - t0);
-  const int nblk = cdiv(ntok, kBlock);
-  const int S = si.S;
   const size_t head_stride = size_t(kBlock) * D;  // elements per (block, head)
-  const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
   // Wave roles: row tile rt and key part kp of every 64-key block.  With at
   // most two row tiles a block is cut into four 16-key parts (so that even a
   // single row tile keeps all four SIMDs busy), else into two 32-key halves.
@@ -618,8 +636,12 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int c = 0; c < QCH; ++c) qv[c] = make_uint4(0, 0, 0, 0);
     }
   }
+  // the parent array (the tree chunk needs it; in a one-sequence launch which
+  // chunk that is is known only with the prefix length, so every chunk reads it)
   int par = -1;
-  if (with_tree && w == 0) par = p.parents[si.off + min(lane, si.T - 1)];
+  if (FUSED && w == 0 && (need_p || it.s == si.S - 1)) par = p.parents[si.off + min(lane, si.T - 1)];
+  int p_read = 0;
+  if (need_p) p_read = p.prefix_lens[0];
   int my_id = -1;
   {
     const int lb = it.s * (p.chunk / kBlock) + lane;
@@ -627,6 +649,18 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
   wait_vm<0>();
+  if (need_p) {
+    const bool p_ok = p_read >= 0 && p_read <= p.max_prefix;
+    if (!p_ok && tid == 0 && it.s == 0 && it.g == 0 && it.rp == 0) set_error(p.hdr, kErrBadPrefix);
+    si.P = p_ok ? p_read : 0;
+    si.S = si.P > 0 ? cdiv(si.P, p.chunk) : 1;
+    if (it.s >= si.S) return;  // a chunk past the actual prefix
+  }
+  const int t0 = it.s * p.chunk;
+  const int ntok = max(0, min(si.P, t0 + p.chunk) - t0);
+  const int nblk = cdiv(ntok, kBlock);
+  const int S = si.S;
+  const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
 
   // ---- tree rows (fused, last chunk only): DMA into LDS, issued before the KV
   // blocks so that waiting for them does not wait for the blocks.  Every
@@ -1155,7 +1189,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int* perm = pl + p.batch;              // [pow2 >= batch]
   const int tid = threadIdx.x;
 
-  const int items = build_table(p, cum, ot, pl, perm, sm.scratch);
+  int items;
+  if (p.single) {
+    items = p.single_items;
+    if (blockIdx.x == 0 && tid == 0 &&
+        (p.tree_offsets[0] != 0 || p.tree_offsets[1] != p.total_nodes))
+      set_error(p.hdr, kErrBadTree);
+  } else {
+    items = build_table(p, cum, ot, pl, perm, sm.scratch);
+  }
 
   // items in increasing order: first blockIdx.x, then from the ticket counter.
   // A workgroup waits only for the other chunks of its own group, whose
@@ -1164,7 +1206,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int li = int(blockIdx.x);
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
-    const Item it = decode_item(p, cum, ot, pl, perm, li);
+    const Item it = p.single ? decode_single(p, li) : decode_item(p, cum, ot, pl, perm, li);
     process_item<T, D, FUSED>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
