@@ -505,6 +505,26 @@ __device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char*
 }
 
 // Wait until at most n of this wave's vector-memory operations are outstanding.
+// A 32-bit global load hidden from the compiler.  Its value is read only
+// after the caller's own wait and `settle`, so the compiler cannot pull a
+// wait for it (or its move to a scalar register) in front of the loads
+// issued after it.
+// kCoherentLoad reads past this XCD's L2, as an agent-scope load does.
+template <bool kCoherentLoad = false>
+__device__ __forceinline__ int hidden_load(const int* ptr) {
+  int v;
+  if constexpr (kCoherentLoad)
+    asm volatile("global_load_dword %0, %1, off sc1" : "=v"(v) : "v"(ptr) : "memory");
+  else
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
+  return v;
+}
+// Ties a hidden load's register to this point (after an s_waitcnt).
+__device__ __forceinline__ int settle(int v) {
+  asm volatile("" : "+v"(v)::"memory");
+  return v;
+}
+
 template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
@@ -619,8 +639,12 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // so no later wait for these values can hold up the transfers.
   unsigned* const counter = p.arrive + size_t(it.grp) * kCounterStride;
   unsigned* const sense = counter + kCounterStride / 2;
-  unsigned sense0 = 0;
-  if (tid == 0) sense0 = ld_counter(sense);
+  // nothing of the previous item is still in flight (free for the first item):
+  // a wait the compiler would otherwise place before reusing registers of the
+  // previous item lands here, not between the loads of this trip
+  wait_vm<0>();
+  int sense_read = 0;  // hidden: a compiler wait for it would stall the loads below
+  if (tid == 0) sense_read = hidden_load<true>(reinterpret_cast<const int*>(sense));
   uint4 qv[QCH];
   {
     const int r = 16 * rt + lr;
@@ -640,8 +664,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // chunk that is is known only with the prefix length, so every chunk reads it)
   int par = -1;
   if (FUSED && w == 0 && (need_p || it.s == si.S - 1)) par = p.parents[si.off + min(lane, si.T - 1)];
-  int p_read = 0;
-  if (need_p) p_read = p.prefix_lens[0];
+  // one-sequence numbering: the prefix length, and (first item only) the two
+  // tree offsets, which must be 0 and N
+  const bool first_of_launch = it.s == 0 && it.g == 0 && it.rp == 0;
+  int p_read = 0, toff = 0;
+  if (need_p) {
+    p_read = hidden_load(p.prefix_lens);
+    if (first_of_launch && w == 0) toff = hidden_load(p.tree_offsets + (lane & 1));
+  }
   int my_id = -1;
   {
     const int lb = it.s * (p.chunk / kBlock) + lane;
@@ -649,9 +679,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
   wait_vm<0>();
+  const unsigned sense0 = unsigned(settle(sense_read));
   if (need_p) {
+    p_read = __builtin_amdgcn_readfirstlane(settle(p_read));  // the same in every lane
+    toff = settle(toff);
+    if (first_of_launch && w == 0 && lane < 2 && toff != (lane == 0 ? 0 : si.T))
+      set_error(p.hdr, kErrBadTree);
     const bool p_ok = p_read >= 0 && p_read <= p.max_prefix;
-    if (!p_ok && tid == 0 && it.s == 0 && it.g == 0 && it.rp == 0) set_error(p.hdr, kErrBadPrefix);
+    if (!p_ok && tid == 0 && first_of_launch) set_error(p.hdr, kErrBadPrefix);
     si.P = p_ok ? p_read : 0;
     si.S = si.P > 0 ? cdiv(si.P, p.chunk) : 1;
     if (it.s >= si.S) return;  // a chunk past the actual prefix
@@ -1191,10 +1226,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
 
   int items;
   if (p.single) {
-    items = p.single_items;
-    if (blockIdx.x == 0 && tid == 0 &&
-        (p.tree_offsets[0] != 0 || p.tree_offsets[1] != p.total_nodes))
-      set_error(p.hdr, kErrBadTree);
+    items = p.single_items;  // the tree offsets are checked by the launch's first item
   } else {
     items = build_table(p, cum, ot, pl, perm, sm.scratch);
   }
