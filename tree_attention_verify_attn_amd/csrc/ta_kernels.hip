@@ -610,7 +610,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform for the compiler too
   const int lr = lane & 15;
   const int kq = lane >> 4;
 
@@ -726,14 +726,11 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   constexpr int SLOTB = Gm::SLOTB;  // K tile, then V tile
   uint32_t doff[KI];
   dma_offsets<T, D>(doff);
-  uint64_t bad = 0;
+  const uint64_t bad = __ballot(lane < nblk && !(my_id >= 0 && my_id < p.num_blocks));
+  if (bad != 0 && tid == 0) set_error(p.hdr, kErrBadPrefix);
   auto issue = [&](int j) {
     int id = __builtin_amdgcn_readfirstlane(__shfl(my_id, j));  // wave-uniform
-    if (!(id >= 0 && id < p.num_blocks)) {
-      if (tid == 0) set_error(p.hdr, kErrBadPrefix);
-      bad |= uint64_t(1) << j;
-      id = 0;
-    }
+    if ((bad >> j) & 1) id = 0;
     unsigned char* slot = ring + (j % NS) * SLOTB;
     const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
     dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot, doff);
@@ -786,9 +783,10 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // visible to a row iff bit j of its node's mask word is set; staged-row
   // reads are clamped to the staging area).  Lane (row lr, group kq) ends up
   // holding scores of keys kp KS + 16 a + 4 kq + i (a < KS / 16, i < 4).
-  auto compute = [&](auto tree_tag, auto ks_tag, const unsigned char* kb, const unsigned char* vb,
-                     int nvalid) {
+  auto compute = [&](auto tree_tag, auto ks_tag, auto mask_tag, const unsigned char* kb,
+                     const unsigned char* vb, int nvalid) {
     constexpr bool kTree = decltype(tree_tag)::value;
+    constexpr bool kMasked = kTree || decltype(mask_tag)::value;  // else every key is visible
     constexpr int KS = decltype(ks_tag)::value;  // 16 or 32 keys
     constexpr int NA = KS / 16;                  // 16-key tiles
     const int kbase = kp * KS;
@@ -856,7 +854,6 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     // running reference max m_run is in scaled units.  Only a partial block or
     // the tree block needs the per-key mask.
     const float c = p.scale_log2;
-    const bool masked = kTree || nvalid < kBlock;
     float sr[NA][4];
     float rmax = -INFINITY;
 #pragma unroll
@@ -864,7 +861,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = sacc[a][i];
-        if (masked) {
+        if constexpr (kMasked) {
           const int tok = kbase + 16 * a + 4 * kq + i;
           const bool vis = kTree ? bool((word >> tok) & 1) : tok < nvalid;
           v = vis ? v : -INFINITY;
@@ -943,32 +940,53 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
           }
     }
   };
-  // the wave's part of one block, with the part size of this item
-  auto run_block = [&](auto tree_tag, const unsigned char* kb, const unsigned char* vb, int nvalid) {
-    if (KP == 4) compute(tree_tag, std::integral_constant<int, 16>{}, kb, vb, nvalid);
-    else compute(tree_tag, std::integral_constant<int, 32>{}, kb, vb, nvalid);
-  };
-
-  // ---- the tree piece, while the first KV blocks are still in flight
-  if (with_tree) {
-    raw_barrier();  // staged rows of every wave and the mask words are in LDS
-    if (active) run_block(std::true_type{}, tk, tv, 0);
-  }
-
-  // ---- stream the chunk through the ring; the DMA of block j + NS starts as
-  // soon as every wave is done with block j
-  for (int j = 0; j < nblk; ++j) {
-    unsigned char* slot = ring + (j % NS) * SLOTB;
-    const int nv = ((bad >> j) & 1) ? 0 : min(kBlock, ntok - j * kBlock);
-    wait_blocks<KI, NSMAX>(min(NS - 1, nblk - 1 - j));
-    raw_barrier();
-    if (nv < kBlock) {
-      clear_tail(slot, nv);
+  // ---- stream blocks [j0, j1) of the chunk through the ring; the DMA of
+  // block j + NS starts as soon as every wave is done with block j.  The part
+  // size, the per-key mask and whether this wave computes at all are fixed
+  // for the whole loop, so the running output stays in place in registers.
+  auto stream = [&](auto ks_tag, auto mask_tag, auto act_tag, int j0, int j1) {
+    constexpr bool kMasked = decltype(mask_tag)::value;
+    for (int j = j0; j < j1; ++j) {
+      unsigned char* slot = ring + (j % NS) * SLOTB;
+      wait_blocks<KI, NSMAX>(min(NS - 1, nblk - 1 - j));
       raw_barrier();
+      int nv = kBlock;
+      if constexpr (kMasked) {
+        nv = ((bad >> j) & 1) ? 0 : min(kBlock, ntok - j * kBlock);
+        if (nv < kBlock) {
+          clear_tail(slot, nv);
+          raw_barrier();
+        }
+      }
+      if constexpr (decltype(act_tag)::value)
+        compute(std::false_type{}, ks_tag, mask_tag, slot, slot + BLKB, nv);
+      raw_barrier();
+      if (j + NS < nblk) issue(j + NS);
     }
-    if (active) run_block(std::false_type{}, slot, slot + BLKB, nv);
-    raw_barrier();
-    if (j + NS < nblk) issue(j + NS);
+  };
+  // the tree piece (while the first KV blocks are still in flight), then the
+  // full blocks without the per-key mask and a partial last block with it;
+  // a chunk with a bad block id takes the masked loop throughout
+  auto tree_and_stream = [&](auto ks_tag, auto act_tag) {
+    if (with_tree) {
+      raw_barrier();  // staged rows of every wave and the mask words are in LDS
+      if constexpr (decltype(act_tag)::value)
+        compute(std::true_type{}, ks_tag, std::true_type{}, tk, tv, 0);
+    }
+    if (bad != 0) {
+      stream(ks_tag, std::true_type{}, act_tag, 0, nblk);
+    } else {
+      const int nfull = ntok / kBlock;
+      stream(ks_tag, std::false_type{}, act_tag, 0, nfull);
+      stream(ks_tag, std::true_type{}, act_tag, nfull, nblk);
+    }
+  };
+  if (KP == 4) {
+    if (active) tree_and_stream(std::integral_constant<int, 16>{}, std::true_type{});
+    else tree_and_stream(std::integral_constant<int, 16>{}, std::false_type{});
+  } else {
+    if (active) tree_and_stream(std::integral_constant<int, 32>{}, std::true_type{});
+    else tree_and_stream(std::integral_constant<int, 32>{}, std::false_type{});
   }
   wait_vm<0>();
   __syncthreads();
