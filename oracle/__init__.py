@@ -5,6 +5,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Python binding) never imports, calls or links anything here, and nothing here
 imports the product path.
 
+``commit.py`` covers the step after verification (greedy acceptance of a
+tree path and committing it into the paged cache), written as the plain
+per-sequence loops of its stated reading.
+
 What it computes is the plain definition: for every tree node and query head,
 unsplit softmax attention over the sequence's whole committed prefix plus the
 tree nodes on that node's root path (itself included).  The split method
@@ -16,6 +20,7 @@ against hand-derived tables, closed forms, a library attention routine and
 invariants.  Numeric values at the five synthetic configs themselves are pinned
 only through those invariants (the pages print no output values).
 """
+from .commit import accept_greedy, commit  # noqa: F401
 from .tree_attention import (  # noqa: F401
     ancestor_or_self_mask,
     build_masks,
