@@ -80,7 +80,8 @@ typedef enum {
   TA_ERR_WORKSPACE = 4,    /* workspace null or smaller than tree_attn_workspace_size */
   TA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
   TA_ERR_BAD_PREFIX = 6,   /* device-detected: prefix length or block id out of range */
-  TA_ERR_TIMEOUT = 7       /* device-detected: a bounded cross-workgroup wait gave up */
+  TA_ERR_TIMEOUT = 7,      /* device-detected: a bounded cross-workgroup wait gave up */
+  TA_ERR_NO_BLOCKS = 8     /* device-detected: free list or block-table row too small */
 } ta_status;
 
 typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
@@ -169,6 +170,64 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
                            const void* v_tree, const int32_t* parents,
                            const int32_t* tree_offsets, void* out, float* lse_out,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Greedy acceptance after verification, one sequence per wave.  For tree
+ * node i of sequence b (local index), draft_tokens[i] is the token the node
+ * stands for and target_argmax[i] the target model's greedy next token at it
+ * (both int32 [N], packed like the tree rows).  A root is accepted; node i is
+ * accepted iff its parent p is and draft_tokens[i] == target_argmax[p].  The
+ * accepted path ends at the deepest accepted node (the smallest index among
+ * equally deep ones) and runs root first:
+ *   accept_len[b]       number of path nodes (>= 1; 0 for an invalid tree)
+ *   accept_path[b][t]   int32 [batch, max_tree_nodes], local node indices,
+ *                       -1 after the path
+ *   bonus_token[b]      target_argmax at the path's last node (-1 if invalid)
+ * Every tree must have 1..max_tree_nodes nodes; a bad parent array or bad
+ * tree_offsets raise TA_ERR_BAD_TREE in the workspace flag.  Only the
+ * workspace header is used: any workspace of at least 768 bytes will do.
+ * [the service commits an accepted path: fdeinterviews.com summary, opening
+ * paragraph; greedy draft decoding: pith.science verdict record, referee
+ * summary.  The pages print no acceptance rule; this is the plain greedy
+ * reading.] */
+ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
+                                  const int32_t* tree_offsets, const int32_t* draft_tokens,
+                                  const int32_t* target_argmax, int32_t* accept_len,
+                                  int32_t* accept_path, int32_t* bonus_token, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* Commit accepted paths into the paged cache.  For every sequence b with
+ * P = prefix_lens[b] and A = accept_len[b] (0 <= A <= tree size; A = 0 commits
+ * nothing), the K/V rows of tree nodes accept_path[b][0..A) (a root path, root
+ * first, as tree_attn_accept_greedy writes it) go, for every KV head, to
+ * prefix positions P .. P+A-1 (slot (P+t) % 64 of block block_table[b][(P+t)/64]),
+ * and prefix_lens[b] becomes P + A.  No other cache slot is written: rejected
+ * nodes leave no trace.  Blocks needed beyond the cdiv(P, 64) the sequence
+ * holds are taken from the front of free_blocks (int32 [free_count], pool
+ * block ids), sequences in batch order, and written into block_table;
+ * *blocks_taken (device int32, may be NULL) receives how many were taken.
+ * Device checks (workspace flag, first error wins):
+ *   - a path that is not a root path of its tree, or bad tree_offsets:
+ *     TA_ERR_BAD_TREE, that sequence is left as it was;
+ *   - P outside [0, 64 * max_blocks_per_seq]: TA_ERR_BAD_PREFIX, likewise;
+ *   - a block-table row too short for P + A, or more blocks needed than
+ *     free_count: TA_ERR_NO_BLOCKS and nothing at all is committed;
+ *   - a free-list entry outside [0, num_blocks): TA_ERR_BAD_PREFIX and
+ *     nothing is committed; an entry of the sequence's own row outside it:
+ *     TA_ERR_BAD_PREFIX, the rows bound for that block are not written.
+ * Uses shape's batch, num_kv_heads, head_dim, dtype, max_blocks_per_seq,
+ * max_tree_nodes, total_tree_nodes and num_blocks.  The workspace must hold at
+ * least tree_attn_workspace_size(shape) bytes (its scratch area holds the
+ * per-sequence plan; the counters are not touched).  Three kernel launches.
+ * [fdeinterviews.com summary, opening paragraph and the paragraph on hidden
+ * correctness obligations; pith.science verdict record, minor comment on
+ * Section 3.3 (KV-cache bookkeeping rewound to the accepted tokens)] */
+ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void* v_tree,
+                           const int32_t* parents, const int32_t* tree_offsets,
+                           const int32_t* accept_len, const int32_t* accept_path,
+                           void* k_cache, void* v_cache, int32_t* block_table,
+                           int32_t* prefix_lens, const int32_t* free_blocks, int32_t free_count,
+                           int32_t* blocks_taken, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /* Synchronises `stream`, reads and clears the device error flag of workspace
  * `ws` and returns it (TA_OK if no kernel flagged anything).  This is the only

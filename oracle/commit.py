@@ -99,7 +99,8 @@ def commit(inp, accept_len, path, free_blocks, free_count: int) -> Dict[str, obj
 
     Returns a dict with the new ``k_cache``, ``v_cache``, ``block_table``,
     ``prefix_lens``, ``blocks_taken`` and ``error`` (0, ``"bad_tree"`` when
-    some path was not a root path -- those sequences are skipped -- or
+    some path was not a root path or ``"bad_prefix"`` when some prefix length
+    was outside [0, 64 * table columns] -- those sequences are skipped -- or
     ``"no_blocks"`` when nothing was committed for lack of blocks).
     """
     B = inp.batch
@@ -126,6 +127,9 @@ def commit(inp, accept_len, path, free_blocks, free_count: int) -> Dict[str, obj
             error = error or "bad_tree"
             continue
         P = int(plen[b])
+        if not 0 <= P <= BLOCK * maxb:
+            error = error or "bad_prefix"
+            continue
         have = -(-P // BLOCK)
         after = -(-(P + A) // BLOCK)
         if after > maxb:

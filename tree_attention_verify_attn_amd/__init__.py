@@ -2,7 +2,9 @@
 
 A draft tree's queries attend to their sequence's committed prefix (paged KV
 cache, no mask) and to the tree tokens on their root path (ancestor-or-self
-mask); the two pieces are merged exactly by log-sum-exp.  All arithmetic runs in
+mask); the two pieces are merged exactly by log-sum-exp.  After verification,
+``accept_greedy`` picks the accepted root path of each tree and ``commit``
+appends its K/V rows to the paged cache.  All arithmetic runs in
 hand-written HIP kernels behind the C ABI of ``libtreeattn.so``
 (``include/tree_attn.h``); this package only marshals arguments.
 """
@@ -10,7 +12,9 @@ from .api import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_F32,
     TreeAttnError,
+    accept_greedy,
     alloc_workspace,
+    commit,
     build_mask,
     get_error,
     make_shape,

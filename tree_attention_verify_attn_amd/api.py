@@ -213,6 +213,60 @@ def verify(shape: Shape, q, k_cache, v_cache, block_table, prefix_lens, k_tree, 
     return out, lse
 
 
+def accept_greedy(shape: Shape, parents, tree_offsets, draft_tokens, target_argmax, workspace,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Greedy path acceptance (tree_attn_accept_greedy): returns accept_len [B],
+    accept_path [B, max_tree_nodes] and bonus_token [B], all int32."""
+    N, B, Tm = shape.total_tree_nodes, shape.batch, shape.max_tree_nodes
+    _want(parents, "parents", torch.int32, (N,))
+    _want(tree_offsets, "tree_offsets", torch.int32, (B + 1,))
+    _want(draft_tokens, "draft_tokens", torch.int32, (N,))
+    _want(target_argmax, "target_argmax", torch.int32, (N,))
+    dev = parents.device
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty(B, Tm, dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(load().tree_attn_accept_greedy(ctypes.byref(shape), _ptr(parents), _ptr(tree_offsets),
+                                          _ptr(draft_tokens), _ptr(target_argmax), _ptr(n),
+                                          _ptr(path), _ptr(bonus), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)),
+           "tree_attn_accept_greedy")
+    return n, path, bonus
+
+
+def commit(shape: Shape, k_tree, v_tree, parents, tree_offsets, accept_len, accept_path,
+           k_cache, v_cache, block_table, prefix_lens, free_blocks, free_count: int, workspace,
+           blocks_taken: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """Commit accepted paths into the paged cache in place (tree_attn_commit).
+    Updates k_cache, v_cache, block_table and prefix_lens; returns blocks_taken
+    (int32 [1]) when given."""
+    N, B, Hkv, D = (shape.total_tree_nodes, shape.batch, shape.num_kv_heads, shape.head_dim)
+    el = _elem(shape)
+    _want(k_tree, "k_tree", el, (N, Hkv, D))
+    _want(v_tree, "v_tree", el, (N, Hkv, D))
+    _want(parents, "parents", torch.int32, (N,))
+    _want(tree_offsets, "tree_offsets", torch.int32, (B + 1,))
+    _want(accept_len, "accept_len", torch.int32, (B,))
+    _want(accept_path, "accept_path", torch.int32, (B, shape.max_tree_nodes))
+    _want(k_cache, "k_cache", el, (shape.num_blocks, Hkv, 64, D))
+    _want(v_cache, "v_cache", el, (shape.num_blocks, Hkv, 64, D))
+    _want(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
+    _want(prefix_lens, "prefix_lens", torch.int32, (B,))
+    if free_count > 0:
+        _want(free_blocks, "free_blocks", torch.int32)
+        if free_blocks.numel() < free_count:
+            raise ValueError("free_blocks holds fewer than free_count entries")
+    if blocks_taken is not None:
+        _want(blocks_taken, "blocks_taken", torch.int32, (1,))
+    _check(load().tree_attn_commit(ctypes.byref(shape), _ptr(k_tree), _ptr(v_tree), _ptr(parents),
+                                   _ptr(tree_offsets), _ptr(accept_len), _ptr(accept_path),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(prefix_lens), _ptr(free_blocks) if free_count > 0 else None,
+                                   int(free_count), _ptr(blocks_taken), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)), "tree_attn_commit")
+    return blocks_taken
+
+
 def get_error(workspace: torch.Tensor, stream=None) -> int:
     """Synchronise the stream, read and clear the device-side error flag."""
     return int(load().tree_attn_get_error(_ptr(workspace), _stream(stream)))

@@ -8,6 +8,7 @@
 #include <unordered_map>
 
 #include "ta_kernels.hip"
+#include "ta_commit.hip"
 #include "tree_attn.h"
 
 namespace ta {
@@ -436,6 +437,86 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
   return static_cast<ta_status>(dispatch_attn<true>(shape, p, L, stream));
 }
 
+ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
+                                  const int32_t* tree_offsets, const int32_t* draft_tokens,
+                                  const int32_t* target_argmax, int32_t* accept_len,
+                                  int32_t* accept_path, int32_t* bonus_token, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!tree_offsets || !accept_len || !accept_path || !bonus_token) return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!parents || !draft_tokens || !target_argmax))
+    return TA_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < sizeof(WsHeader)) return TA_ERR_WORKSPACE;
+  AcceptParams a{};
+  a.parents = parents;
+  a.tree_offsets = tree_offsets;
+  a.draft = draft_tokens;
+  a.argmax = target_argmax;
+  a.accept_len = accept_len;
+  a.path = accept_path;
+  a.bonus = bonus_token;
+  a.hdr = static_cast<WsHeader*>(ws);
+  a.batch = shape->batch;
+  a.total_nodes = shape->total_tree_nodes;
+  a.max_tree = shape->max_tree_nodes;
+  hipLaunchKernelGGL(accept_kernel, dim3(unsigned(cdiv(shape->batch, kAcceptWaves))),
+                     dim3(64 * kAcceptWaves), 0, stream, a);
+  return static_cast<ta_status>(launch_status());
+}
+
+ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void* v_tree,
+                           const int32_t* parents, const int32_t* tree_offsets,
+                           const int32_t* accept_len, const int32_t* accept_path,
+                           void* k_cache, void* v_cache, int32_t* block_table,
+                           int32_t* prefix_lens, const int32_t* free_blocks, int32_t free_count,
+                           int32_t* blocks_taken, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens)
+    return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!parents || !k_tree || !v_tree)) return TA_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache || shape->num_blocks < 1) return TA_ERR_INVALID_ARG;
+  if (free_count < 0 || (free_count > 0 && !free_blocks)) return TA_ERR_INVALID_ARG;
+  if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_cache) || !aligned16(v_cache))
+    return TA_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return TA_ERR_WORKSPACE;
+  const WsLayout L = layout_for(shape, kBlock);
+  const size_t plan_bytes = sizeof(CommitPlan) * size_t(shape->batch) + 256;
+  if (ws_bytes < L.partial_off + plan_bytes) return TA_ERR_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  CommitParams c{};
+  c.k_tree = k_tree;
+  c.v_tree = v_tree;
+  c.parents = parents;
+  c.tree_offsets = tree_offsets;
+  c.accept_len = accept_len;
+  c.path = accept_path;
+  c.k_cache = k_cache;
+  c.v_cache = v_cache;
+  c.block_table = block_table;
+  c.prefix_lens = prefix_lens;
+  c.free_blocks = free_blocks;
+  c.blocks_taken = blocks_taken;
+  c.hdr = reinterpret_cast<WsHeader*>(w);
+  c.go = reinterpret_cast<int*>(w + L.partial_off);
+  c.plan = reinterpret_cast<CommitPlan*>(w + L.partial_off + 256);
+  c.batch = shape->batch;
+  c.total_nodes = shape->total_tree_nodes;
+  c.max_tree = shape->max_tree_nodes;
+  c.max_blocks = shape->max_blocks_per_seq;
+  c.num_blocks = shape->num_blocks;
+  c.hkv = shape->num_kv_heads;
+  c.row_bytes = shape->head_dim * (shape->dtype == TA_DTYPE_BF16 ? 2 : 4);
+  c.free_count = free_count;
+  hipLaunchKernelGGL(commit_check_kernel, dim3(unsigned(cdiv(shape->batch, kAcceptWaves))),
+                     dim3(64 * kAcceptWaves), 0, stream, c);
+  hipLaunchKernelGGL(commit_alloc_kernel, dim3(1), dim3(kAttnThreads), 0, stream, c);
+  hipLaunchKernelGGL(commit_copy_kernel, dim3(unsigned(shape->batch)), dim3(kThreads), 0, stream, c);
+  return static_cast<ta_status>(launch_status());
+}
+
 ta_status tree_attn_get_error(void* ws, hipStream_t stream) {
   if (!ws) return TA_ERR_INVALID_ARG;
   int err = 0;
@@ -461,6 +542,7 @@ const char* tree_attn_status_string(ta_status status) {
     case TA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case TA_ERR_BAD_PREFIX: return "prefix length or KV block id out of range (device check)";
     case TA_ERR_TIMEOUT: return "a bounded cross-workgroup wait gave up (device check)";
+    case TA_ERR_NO_BLOCKS: return "free list or block-table row too small for the commit (device check)";
   }
   return "unknown status";
 }

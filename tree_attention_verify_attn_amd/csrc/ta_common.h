@@ -30,6 +30,7 @@ enum : int {
   kErrHip = 5,
   kErrBadPrefix = 6,
   kErrTimeout = 7,
+  kErrNoBlocks = 8,
 };
 
 constexpr int kCounterStride = 64;  // unsigned words between two counters: one 256-byte line each
