@@ -23,6 +23,8 @@ Timing protocol
   the kernel's average duration plus the (sub-0.1 us) gap between queued
   launches; value = algorithmic bytes / ms_per_step.
 * cpu_baseline: the fp64 NumPy oracle on the same workload, on this host.
+* after_verify: greedy acceptance and the commit of the accepted paths into the
+  paged cache, timed on a 256-sequence batch (see bench_after_verify).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -143,6 +145,114 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
     }
 
 
+def bench_after_verify(ta, torch, np, steps: int) -> dict:
+    """Greedy acceptance and commit timed on a 256-sequence batch with the
+    ragged workload's tree mix (1-node / chain-4 / 12-node at 0.2/0.5/0.3),
+    32 query / 8 KV heads, head dim 128, bf16.  Prefix lengths are the ragged
+    workload's draws modulo 128 (the commit touches only the blocks at the
+    prefix end, so the block-boundary mix is what matters).  Acceptance: K
+    calls back to back between two events.  Commit: each call is bracketed by
+    its own events after the block table and prefix lengths are restored, so
+    every call appends the same rows; median reported.  A spin kernel holds
+    the GPU while the host queues the timed calls, so host overhead is not
+    timed."""
+    from workloads import TREE_12, TREE_CHAIN4, TREE_SINGLE, free_list, make_inputs, make_tokens
+    rng = np.random.default_rng(1005)
+    B = 256
+    z = rng.standard_normal(B)
+    lens = (np.clip(np.rint(np.exp(np.log(2048.0) + z)), 16, 32768).astype(np.int64) % 128)
+    kinds = rng.choice(3, size=B, p=[0.2, 0.5, 0.3])
+    trees = [(TREE_SINGLE, TREE_CHAIN4, TREE_12)[k] for k in kinds]
+    inp = make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      prefix_lens=lens, trees=trees, rng=rng, spare_blocks=2 * B,
+                      extra_table_cols=1)
+    draft, argmax = make_tokens(inp.parents, inp.tree_offsets, rng, p_match=0.7, vocab=32000)
+    free = free_list(inp, rng)
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(
+                torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    shape = ta.make_shape(batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          max_blocks_per_seq=inp.max_blocks_per_seq, max_tree_nodes=12,
+                          max_prefix_len=inp.max_prefix_len, total_tree_nodes=inp.total_tree_nodes,
+                          num_blocks=inp.num_blocks, dtype=ta.DTYPE_BF16)
+    ws = ta.alloc_workspace(shape)
+    par, off = dev(inp.parents), dev(inp.tree_offsets)
+    dr, am = dev(draft), dev(argmax)
+    kt, vt = dev(inp.k_tree), dev(inp.v_tree)
+    kc, vc = dev(inp.k_cache), dev(inp.v_cache)
+    table0, plen0 = dev(inp.block_table), dev(inp.prefix_lens)
+    table, plen = table0.clone(), plen0.clone()
+    freed = dev(free)
+    taken = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib = ta._lib.load()
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    path = torch.empty(B, 12, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    acc_args = (ctypes.byref(shape), par.data_ptr(), off.data_ptr(), dr.data_ptr(), am.data_ptr(),
+                n.data_ptr(), path.data_ptr(), bonus.data_ptr(), ws.data_ptr(), ws.numel(), sh)
+    com_args = (ctypes.byref(shape), kt.data_ptr(), vt.data_ptr(), par.data_ptr(), off.data_ptr(),
+                n.data_ptr(), path.data_ptr(), kc.data_ptr(), vc.data_ptr(), table.data_ptr(),
+                plen.data_ptr(), freed.data_ptr(), len(free), taken.data_ptr(), ws.data_ptr(),
+                ws.numel(), sh)
+
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    per_cycle_ms = max(c0.elapsed_time(c1), 1e-3) / 1_000_000
+
+    def hold():  # keep the GPU busy while the host queues the timed calls (~100 us each)
+        torch.cuda._sleep(int(0.1 * steps / per_cycle_ms))
+
+    for _ in range(5):
+        lib.tree_attn_accept_greedy(*acc_args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold()
+    e0.record()
+    for _ in range(steps):
+        lib.tree_attn_accept_greedy(*acc_args)
+    e1.record()
+    torch.cuda.synchronize()
+    accept_us = e0.elapsed_time(e1) * 1e3 / steps
+    rows = int(n.sum().item())
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for _ in range(3):
+        table.copy_(table0)
+        plen.copy_(plen0)
+        lib.tree_attn_commit(*com_args)
+    torch.cuda.synchronize()
+    hold()
+    for a, b in evs:
+        table.copy_(table0)
+        plen.copy_(plen0)
+        a.record()
+        lib.tree_attn_commit(*com_args)
+        b.record()
+    torch.cuda.synchronize()
+    commit_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    err = ta.get_error(ws)
+    if err != 0:
+        raise RuntimeError(f"device error in acceptance/commit: {ta.status_string(err)}")
+    moved = 2 * rows * 8 * 128 * 2  # K and V rows read and written once each
+    return {
+        "workload": "256 sequences, tree mix 1/chain-4/12 (0.2/0.5/0.3), Hkv 8, D 128, bf16",
+        "accept_greedy_us": round(accept_us, 3),
+        "commit_us": round(commit_us, 3),
+        "commit_rows": rows,
+        "commit_blocks_taken": int(taken.item()),
+        "commit_row_bytes_moved": 2 * moved,
+        "commit_GBps": round(2 * moved / (commit_us * 1e-6) / 1e9, 2),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +265,8 @@ def main() -> int:
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-after-verify", action="store_true",
+                    help="skip timing greedy acceptance and the cache commit")
     ap.add_argument("--copy-bytes", type=float, default=0.0,
                     help="instead of the benchmark, run --steps plain device-to-device copies "
                          "of this many bytes (reference for the HBM traffic counters)")
@@ -352,6 +464,9 @@ def main() -> int:
         },
         "host_wall_s": round(t_host, 3),
     }
+    if not args.no_after_verify:
+        log("acceptance and commit (after-verify step)")
+        result["after_verify"] = bench_after_verify(ta, torch, np, 50)
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, nbytes)

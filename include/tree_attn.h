@@ -217,7 +217,7 @@ ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
  * Uses shape's batch, num_kv_heads, head_dim, dtype, max_blocks_per_seq,
  * max_tree_nodes, total_tree_nodes and num_blocks.  The workspace must hold at
  * least tree_attn_workspace_size(shape) bytes (its scratch area holds the
- * per-sequence plan; the counters are not touched).  Three kernel launches.
+ * per-sequence plan; the counters are not touched).  Two kernel launches.
  * [fdeinterviews.com summary, opening paragraph and the paragraph on hidden
  * correctness obligations; pith.science verdict record, minor comment on
  * Section 3.3 (KV-cache bookkeeping rewound to the accepted tokens)] */

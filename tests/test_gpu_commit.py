@@ -268,3 +268,18 @@ def test_commit_full_size_ragged_batch_properties():
             blk = table[b, pos // 64]
             assert np.array_equal(kc[blk, :, pos % 64], _host_bits(inp.k_cache)[blk, :, pos % 64])
     assert taken == nxt
+
+
+def test_commit_bad_prefix_length_skips_only_that_sequence():
+    import tree_attention_verify_attn_amd as ta
+    inp, draft, argmax, free = _batch(76, [TREE_CHAIN4, TREE_12, TREE_CHAIN4], [10, 64, 5],
+                                      p_match=1.0)
+    n, path, _ = oracle.accept_greedy(inp.parents, inp.tree_offsets, draft, argmax, 12)
+    inp.prefix_lens[1] = 64 * inp.max_blocks_per_seq + 1    # beyond the table row
+    want = oracle.commit(inp, n, path, free, len(free))
+    assert want["error"] == "bad_prefix"
+    d = to_device(inp, max_prefix_len=0)
+    say("commit: one prefix length beyond its table row")
+    taken = _commit_gpu(inp, d, n, path, free, len(free))
+    assert ta.get_error(d.workspace) == 6
+    _check_commit(inp, d, want, taken, "bad prefix")

@@ -483,7 +483,7 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
     return TA_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return TA_ERR_WORKSPACE;
   const WsLayout L = layout_for(shape, kBlock);
-  const size_t plan_bytes = sizeof(CommitPlan) * size_t(shape->batch) + 256;
+  const size_t plan_bytes = sizeof(CommitPlan) * size_t(shape->batch);
   if (ws_bytes < L.partial_off + plan_bytes) return TA_ERR_WORKSPACE;
   char* w = static_cast<char*>(ws);
   CommitParams c{};
@@ -500,8 +500,7 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
   c.free_blocks = free_blocks;
   c.blocks_taken = blocks_taken;
   c.hdr = reinterpret_cast<WsHeader*>(w);
-  c.go = reinterpret_cast<int*>(w + L.partial_off);
-  c.plan = reinterpret_cast<CommitPlan*>(w + L.partial_off + 256);
+  c.plan = reinterpret_cast<CommitPlan*>(w + L.partial_off);
   c.batch = shape->batch;
   c.total_nodes = shape->total_tree_nodes;
   c.max_tree = shape->max_tree_nodes;
@@ -512,8 +511,7 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
   c.free_count = free_count;
   hipLaunchKernelGGL(commit_check_kernel, dim3(unsigned(cdiv(shape->batch, kAcceptWaves))),
                      dim3(64 * kAcceptWaves), 0, stream, c);
-  hipLaunchKernelGGL(commit_alloc_kernel, dim3(1), dim3(kAttnThreads), 0, stream, c);
-  hipLaunchKernelGGL(commit_copy_kernel, dim3(unsigned(shape->batch)), dim3(kThreads), 0, stream, c);
+  hipLaunchKernelGGL(commit_apply_kernel, dim3(unsigned(shape->batch)), dim3(kThreads), 0, stream, c);
   return static_cast<ta_status>(launch_status());
 }
 

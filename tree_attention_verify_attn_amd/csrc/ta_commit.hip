@@ -16,13 +16,13 @@
 // a wave max over depth * 64 + (63 - node).  Its ancestor-or-self word, read
 // in increasing bit order, is the path root first (parents precede children).
 //
-// Commit, three launches on the stream:
+// Commit, two launches on the stream:
 //   1. commit_check: one wave per sequence validates the path (lane t checks
 //      step t) and records (P, A, blocks needed) in the workspace plan;
-//   2. commit_alloc: one workgroup scans the needs, checks the free list and
-//      the table rows, writes the new block-table entries and prefix lengths;
-//   3. commit_copy: one workgroup per sequence copies the accepted rows of
-//      every KV head into their cache slots (16-byte lane accesses).
+//   2. commit_apply: one workgroup per sequence reads every plan, decides
+//      (identically in all workgroups) whether the free list and the table
+//      rows suffice, takes its blocks, advances its prefix length and copies
+//      its accepted rows of every KV head into their cache slots.
 // (included by ta_api.hip after ta_kernels.hip)
 
 namespace ta {
@@ -50,8 +50,15 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) accept_kernel(AcceptParams 
   const int T = o1 - o0;
   int32_t* path = a.path + size_t(b) * a.max_tree;
   bool bad = !(o0 >= 0 && o1 > o0 && o1 <= a.total_nodes && T <= a.max_tree);
+  // one memory trip for everything per node
+  int par = -1, draft = 0, amax = 0;
+  if (!bad && lane < T) {
+    par = a.parents[o0 + lane];
+    draft = a.draft[o0 + lane];
+    amax = a.argmax[o0 + lane];
+  }
   uint64_t anc = 0;
-  if (!bad) anc = tree_mask_wave(a.parents + o0, T, bad);
+  if (!bad) anc = tree_mask_lanes(par, T, bad);
   if (bad) {
     if (lane == 0) {
       set_error(a.hdr, kErrBadTree);
@@ -60,12 +67,6 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) accept_kernel(AcceptParams 
     }
     if (lane < a.max_tree) path[lane] = -1;
     return;
-  }
-  int par = -1, draft = 0, amax = 0;
-  if (lane < T) {
-    par = a.parents[o0 + lane];
-    draft = a.draft[o0 + lane];
-    amax = a.argmax[o0 + lane];
   }
   const int parent_amax = __shfl(amax, par >= 0 ? par : lane);
   const bool good = lane < T && (par < 0 || draft == parent_amax);
@@ -93,7 +94,7 @@ struct CommitPlan {  // per sequence, in the workspace
   int P;     // prefix length before the commit
   int A;     // rows to append (0 when the sequence is skipped)
   int need;  // new blocks
-  int base;  // first free-list entry it takes
+  int skip;  // 1: the sequence is left as it was (bad path or prefix length)
 };
 
 struct CommitParams {
@@ -111,7 +112,6 @@ struct CommitParams {
   int32_t* blocks_taken;
   WsHeader* hdr;
   CommitPlan* plan;  // [batch]
-  int* go;           // 1 when the allocation succeeded (written by commit_alloc)
   int batch, total_nodes, max_tree, max_blocks, num_blocks, hkv, row_bytes, free_count;
 };
 
@@ -145,74 +145,76 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) commit_check_kernel(CommitP
     const int have = cdiv(pl.P, kBlock);
     const int after = cdiv(pl.P + pl.A, kBlock);
     pl.need = after <= c.max_blocks ? after - have : -1;
-    pl.base = 0;
+    pl.skip = !(ok && p_ok);
     c.plan[b] = pl;
   }
 }
 
-// 2. one workgroup of kAttnThreads: exclusive scan of the needs; when every
-// row fits and the free list covers the total, each sequence takes its blocks
-// from the front of the free list (batch order) and its prefix length grows.
-__global__ void __launch_bounds__(kAttnThreads) commit_alloc_kernel(CommitParams c) {
-  __shared__ int scratch[kAttnWaves];
-  __shared__ int flags[2];
-  const int tid = threadIdx.x;
-  const int per = cdiv(c.batch, kAttnThreads);
-  const int b0 = min(c.batch, tid * per);
-  const int b1 = min(c.batch, b0 + per);
-  int mine = 0;
-  bool fits = true;
-  for (int b = b0; b < b1; ++b) {
-    const int nd = c.plan[b].need;
-    fits = fits && nd >= 0;
-    mine += max(nd, 0);
-  }
-  if (tid == 0) flags[0] = flags[1] = 0;
-  __syncthreads();
-  if (!fits) flags[0] = 1;
-  int total = 0;
-  int base = block_exclusive_scan(mine, scratch, total);  // has barriers: flags[0] is settled
-  const bool go = flags[0] == 0 && total <= c.free_count;
-  // every block id taken must be a valid pool block
-  if (go) {
-    for (int k = tid; k < total; k += kAttnThreads) {
-      const int id = c.free_blocks[k];
-      if (!(id >= 0 && id < c.num_blocks)) flags[1] = 1;
-    }
-  }
-  __syncthreads();
-  const bool ids_ok = flags[1] == 0;
-  if (tid == 0) {
-    if (!go) set_error(c.hdr, kErrNoBlocks);
-    else if (!ids_ok) set_error(c.hdr, kErrBadPrefix);
-    *c.go = go && ids_ok ? 1 : 0;
-    if (c.blocks_taken) *c.blocks_taken = go && ids_ok ? total : 0;
-  }
-  if (!(go && ids_ok)) return;
-  for (int b = b0; b < b1; ++b) {
-    CommitPlan pl = c.plan[b];
-    const int have = cdiv(pl.P, kBlock);
-    for (int k = 0; k < pl.need; ++k)
-      c.block_table[size_t(b) * c.max_blocks + have + k] = c.free_blocks[base + k];
-    pl.base = base;
-    base += pl.need;
-    c.plan[b] = pl;
-    c.prefix_lens[b] = pl.P + pl.A;
-  }
-}
-
-// 3. one workgroup per sequence: row (t, head g, K or V) of the accepted path
-// goes to slot (P + t) % 64 of block block_table[b][(P + t) / 64]; 16 bytes
-// per lane.
-__global__ void __launch_bounds__(kThreads) commit_copy_kernel(CommitParams c) {
+// 2. one workgroup per sequence.  Every workgroup reads all the plans and
+// takes the same decision: the commit goes ahead when every row fits and the
+// free list covers the total need with valid block ids.  Workgroup b then
+// takes its blocks from free-list entries [base_b, base_b + need_b), base_b
+// being the needs of the sequences before it, writes them into its table row,
+// advances its prefix length and copies its accepted rows: row (t, head g,
+// K or V) goes to slot (P + t) % 64 of the block holding position P + t;
+// 16 bytes per lane.
+__global__ void __launch_bounds__(kThreads) commit_apply_kernel(CommitParams c) {
+  __shared__ int red[3][kThreads / 64];
   const int b = blockIdx.x;
-  if (*c.go == 0) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  int before = 0, total = 0, bad_need = 0;
+  for (int x = tid; x < c.batch; x += kThreads) {
+    const int nd = c.plan[x].need;
+    bad_need |= nd < 0;
+    total += max(nd, 0);
+    before += x < b ? max(nd, 0) : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    before += __shfl_xor(before, d);
+    total += __shfl_xor(total, d);
+    bad_need |= __shfl_xor(bad_need, d);
+  }
+  if (lane == 0) {
+    red[0][w] = before;
+    red[1][w] = total;
+    red[2][w] = bad_need;
+  }
+  __syncthreads();
+  before = total = bad_need = 0;
+#pragma unroll
+  for (int x = 0; x < kThreads / 64; ++x) {
+    before += red[0][x];
+    total += red[1][x];
+    bad_need |= red[2][x];
+  }
+  const bool go = !bad_need && total <= c.free_count;
+  int bad_id = 0;
+  if (go)
+    for (int k = tid; k < total; k += kThreads) {
+      const int id = c.free_blocks[k];
+      bad_id |= !(id >= 0 && id < c.num_blocks);
+    }
+  bad_id = __syncthreads_or(bad_id);
+  const bool commit = go && !bad_id;
+  if (b == 0 && tid == 0) {
+    if (!go) set_error(c.hdr, kErrNoBlocks);
+    else if (bad_id) set_error(c.hdr, kErrBadPrefix);
+    if (c.blocks_taken) *c.blocks_taken = commit ? total : 0;
+  }
+  if (!commit) return;
   const CommitPlan pl = c.plan[b];
-  if (pl.A == 0) return;
+  const int have = cdiv(pl.P, kBlock);
+  int32_t* row = c.block_table + size_t(b) * c.max_blocks;
+  for (int k = tid; k < pl.need; k += kThreads) row[have + k] = c.free_blocks[before + k];
+  if (pl.skip || pl.A == 0) return;
+  if (tid == 0) c.prefix_lens[b] = pl.P + pl.A;
   const int o0 = c.tree_offsets[b];
-  const int chunks = c.row_bytes / 16;  // per row
+  const int chunks = c.row_bytes / 16;   // per row
   const int per_t = 2 * c.hkv * chunks;  // K and V rows of one token
-  for (int u = threadIdx.x; u < pl.A * per_t; u += kThreads) {
+  for (int u = tid; u < pl.A * per_t; u += kThreads) {
     const int t = u / per_t;
     int r = u % per_t;
     const int kv = r / (c.hkv * chunks);
@@ -221,7 +223,8 @@ __global__ void __launch_bounds__(kThreads) commit_copy_kernel(CommitParams c) {
     const int ch = r % chunks;
     const int node = c.path[size_t(b) * c.max_tree + t];
     const int pos = pl.P + t;
-    const int blk = c.block_table[size_t(b) * c.max_blocks + pos / kBlock];
+    const int idx = pos / kBlock;
+    const int blk = idx < have ? row[idx] : c.free_blocks[before + idx - have];
     if (!(blk >= 0 && blk < c.num_blocks)) {
       set_error(c.hdr, kErrBadPrefix);
       continue;

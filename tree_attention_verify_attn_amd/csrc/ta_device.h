@@ -100,12 +100,13 @@ __device__ __forceinline__ void set_error(WsHeader* h, int code) {
 // parent is neither -1 nor an earlier node; such a parent is treated as -1.
 // [tree mask of the draft-token piece: pith.science review of arXiv
 // 2508.08192, "What carries the argument"; ancestor-or-self as in SpecInfer]
-__device__ __forceinline__ uint64_t tree_mask_wave(const int32_t* parents, int T, bool& bad) {
+// The same from parent values already in registers (lane i holds node i's
+// parent; lanes >= T are ignored).
+__device__ __forceinline__ uint64_t tree_mask_lanes(int p, int T, bool& bad) {
   const int lane = threadIdx.x & 63;
   int up = -1;
   bool lane_bad = false;
   if (lane < T) {
-    int p = parents[lane];
     lane_bad = !(p == -1 || (p >= 0 && p < lane));
     up = lane_bad ? -1 : p;
   }
@@ -123,6 +124,11 @@ __device__ __forceinline__ uint64_t tree_mask_wave(const int32_t* parents, int T
   }
   bad = __any(lane_bad);
   return anc;
+}
+
+__device__ __forceinline__ uint64_t tree_mask_wave(const int32_t* parents, int T, bool& bad) {
+  const int lane = threadIdx.x & 63;
+  return tree_mask_lanes(lane < T ? parents[lane] : -1, T, bad);
 }
 
 __device__ __forceinline__ uint64_t low_bits(int T) {
