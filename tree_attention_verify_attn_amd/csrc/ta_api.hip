@@ -158,7 +158,21 @@ int choose_chunk(const ta_shape* s, bool fused) {
   return chunk;
 }
 
-WsLayout layout_for(const ta_shape* s, int chunk) {
+// One sequence whose tree is every row of q: items are numbered without a
+// sequence table (and the chunk is the host's).
+bool one_sequence(const ta_shape* s) {
+  return s->batch == 1 && s->total_tree_nodes >= 1 && s->total_tree_nodes <= s->max_tree_nodes;
+}
+
+// The kernel picks the chunk from the actual prefix lengths unless the caller
+// fixed it or the launch numbers items without a table.
+bool chunk_auto(const ta_shape* s) { return s->split_tokens == 0 && !one_sequence(s); }
+
+// Item slots a launch may use beyond groups x chunks-per-group: with the
+// kernel's own chunk every item fits in the grid's first round.
+int auto_cap(const ta_shape* s, bool fused) { return chunk_auto(s) ? grid_capacity(s, fused) : 0; }
+
+WsLayout layout_for(const ta_shape* s, int chunk, int min_item_slots = 0) {
   WsLayout L{};
   const int G = group_of(s);
   const int D = s->head_dim;
@@ -172,6 +186,7 @@ WsLayout layout_for(const ta_shape* s, int chunk) {
   L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
   // large batches: dense per-XCD numbering from a prefix table; small: static
   L.item_slots = L.num_groups * L.s_max;
+  if (L.item_slots < min_item_slots) L.item_slots = min_item_slots;
   L.arrive_off = sizeof(WsHeader);
   L.partial_off = align256(L.arrive_off + sizeof(unsigned) * kCounterStride * size_t(L.num_groups));
   L.total = L.partial_off +
@@ -199,7 +214,8 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.s_max = L.s_max;
   p.item_slots = L.item_slots;
   // one sequence whose tree is every row of q: no sequence table needed
-  p.single = (s->batch == 1 && s->total_tree_nodes >= 1 && s->total_tree_nodes <= s->max_tree_nodes) ? 1 : 0;
+  p.single = one_sequence(s) ? 1 : 0;
+  p.chunk_auto = chunk_auto(s) ? 1 : 0;
   p.single_items = p.single ? s->num_kv_heads * cdiv(s->total_tree_nodes * p.group, kRowsPerPass) * L.s_max : 0;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
   p.scale_log2 = scale * kLog2e;
@@ -279,8 +295,8 @@ extern "C" {
 
 size_t tree_attn_workspace_size(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
-  const size_t a = layout_for(shape, choose_chunk(shape, true)).total;
-  const size_t b = layout_for(shape, choose_chunk(shape, false)).total;
+  const size_t a = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true)).total;
+  const size_t b = layout_for(shape, choose_chunk(shape, false), auto_cap(shape, false)).total;
   return a > b ? a : b;
 }
 
@@ -330,7 +346,7 @@ ta_status tree_attn_prefix(const ta_shape* shape, const void* q, const void* k_c
   if (shape->max_prefix_len > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_prefix))
     return TA_ERR_INVALID_ARG;
-  WsLayout L = layout_for(shape, choose_chunk(shape, false));
+  WsLayout L = layout_for(shape, choose_chunk(shape, false), auto_cap(shape, false));
   st = check_ws(shape, L, ws, ws_bytes);
   if (st != kOk) return static_cast<ta_status>(st);
   if (shape->total_tree_nodes == 0) return TA_OK;
@@ -418,7 +434,7 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
       !aligned16(v_tree))
     return TA_ERR_INVALID_ARG;
-  WsLayout L = layout_for(shape, choose_chunk(shape, true));
+  WsLayout L = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true));
   st = check_ws(shape, L, ws, ws_bytes);
   if (st != kOk) return static_cast<ta_status>(st);
   if (shape->total_tree_nodes == 0) return TA_OK;

@@ -19,6 +19,7 @@ constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row 
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 constexpr int kMaxRingSlots = 3;       // KV blocks the attention kernel keeps in LDS
+constexpr int kMaxChunk = 4096;        // prefix tokens per work item, at most
 
 // Status codes, identical to ta_status in include/tree_attn.h.
 enum : int {
@@ -82,6 +83,7 @@ struct Params {
   int num_groups;            // batch * hkv * rp_max
   int s_max;                 // chunks per group, upper bound
   int item_slots;            // num_groups * s_max: bound on item numbers
+  int chunk_auto;            // 1: the kernel may pick the chunk from the actual prefix lengths
   int single;                // 1: one sequence, items numbered without a table
   int single_items;          // item count of a one-sequence launch
   int first_round;           // workgroups in the grid

@@ -129,7 +129,41 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
   return before + inc - v;
 }
 
-__device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* perm, int* scratch) {
+// Sums of a and b and the max of c over the workgroup's threads; every
+// thread must call it.  Two barriers.
+__device__ __forceinline__ void block_sum2_max(int& a, int& b, int& c, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a += __shfl_xor(a, d);
+    b += __shfl_xor(b, d);
+    c = max(c, __shfl_xor(c, d));
+  }
+  if (lane == 0) {
+    scratch[w] = a;
+    scratch[kAttnWaves + w] = b;
+    scratch[2 * kAttnWaves + w] = c;
+  }
+  __syncthreads();
+  a = b = c = 0;
+#pragma unroll
+  for (int x = 0; x < kAttnWaves; ++x) {
+    a += scratch[x];
+    b += scratch[kAttnWaves + x];
+    c = max(c, scratch[2 * kAttnWaves + x]);
+  }
+  __syncthreads();
+}
+
+// When the host leaves the chunk to the kernel (p.chunk_auto) and the groups
+// (sequence, KV head, row pass) are fewer than the grid's workgroups, the
+// chunk comes from the actual prefix lengths: the smallest multiple of 64
+// tokens with which every item fits in the first round (the sum of the
+// groups' chunk counts stays within the grid) and no group has more than
+// kMaxSplits chunks.  `chunk` returns the chunk in force.
+__device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* perm, int* scratch,
+                           int& chunk) {
   const int tid = threadIdx.x;
   const int n = p.batch;
   const int per = cdiv(n, kAttnThreads);
@@ -138,20 +172,40 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
   const bool flag = blockIdx.x == 0;
   // facts in index order, the item prefix in index order
   constexpr int kPerMax = kMaxBatch / kAttnThreads;
-  int items_q[kPerMax];
-  int local = 0;
+  int items_q[kPerMax], groups_q[kPerMax], p_q[kPerMax];
+  int work = 0, groups = 0, max_blocks = 0;
 #pragma unroll
   for (int q = 0; q < kPerMax; ++q) {
     const int j = j0 + q;
-    items_q[q] = 0;
+    groups_q[q] = 0;
+    p_q[q] = 0;
     if (j < j1) {
       const SeqInfo si = seq_info(p, j, flag);
       ot[j] = int(unsigned(si.off) | (unsigned(si.T) << kTreeSizeShift));
       pl[j] = si.P;
       perm[j] = j;
-      items_q[q] = si.items;
-      local += si.items;
+      groups_q[q] = p.hkv * si.RP;
+      p_q[q] = si.P;
+      const int nb = cdiv(si.P, kBlock);
+      work += groups_q[q] * nb;
+      groups += groups_q[q];
+      max_blocks = max(max_blocks, nb);
     }
+  }
+  chunk = p.chunk;
+  if (p.chunk_auto) {
+    block_sum2_max(work, groups, max_blocks, scratch);
+    if (groups < p.first_round) {
+      int cb = max(cdiv(work, p.first_round - groups), cdiv(max_blocks, kMaxSplits));
+      cb = min(max(cb, 1), kMaxChunk / kBlock);
+      chunk = cb * kBlock;
+    }
+  }
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < kPerMax; ++q) {
+    items_q[q] = groups_q[q] * (p_q[q] > 0 ? cdiv(p_q[q], chunk) : 1);
+    local += items_q[q];
   }
   int total = 0;
   int run = block_exclusive_scan(local, scratch, total);
@@ -206,7 +260,7 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
         g_pl[q] = pl[j];
         const int P = g_pl[q];
         const int T = int(unsigned(g_ot[q]) >> kTreeSizeShift);
-        items_q[q] = p.hkv * cdiv(T * p.group, kRowsPerPass) * (P > 0 ? cdiv(P, p.chunk) : 1);
+        items_q[q] = p.hkv * cdiv(T * p.group, kRowsPerPass) * (P > 0 ? cdiv(P, chunk) : 1);
         local += items_q[q];
       }
     }
@@ -233,6 +287,7 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
 
 struct Item {
   int b, g, rp, s, grp;
+  int chunk;  // prefix tokens per item of this launch
   SeqInfo si;
 };
 
@@ -240,9 +295,11 @@ struct Item {
 // facts from the LDS table, without any global-memory read.  Items are
 // numbered sequence by sequence, then KV head, row pass and chunk (chunk
 // fastest), so the chunks of a group have consecutive numbers.
-__device__ __forceinline__ Item decode_item(const Params& p, const int* cum, const int* ot,
-                                            const int* pl, const int* perm, int li) {
+__device__ __forceinline__ Item decode_item(const Params& p, int chunk, const int* cum,
+                                            const int* ot, const int* pl, const int* perm,
+                                            int li) {
   Item it;
+  it.chunk = chunk;
   int lo = 0, hi = p.batch;  // largest b with cum[b] <= li
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -253,7 +310,7 @@ __device__ __forceinline__ Item decode_item(const Params& p, const int* cum, con
   it.si.off = int(o & ((1u << kTreeSizeShift) - 1u));
   it.si.T = int(o >> kTreeSizeShift);
   it.si.P = pl[lo];
-  it.si.S = it.si.P > 0 ? cdiv(it.si.P, p.chunk) : 1;
+  it.si.S = it.si.P > 0 ? cdiv(it.si.P, chunk) : 1;
   it.si.RP = cdiv(it.si.T * p.group, kRowsPerPass);
   it.si.items = cum[lo + 1] - cum[lo];
   const int local = li - cum[lo];
@@ -272,6 +329,7 @@ __device__ __forceinline__ Item decode_item(const Params& p, const int* cum, con
 // actual prefix turns out empty.
 __device__ __forceinline__ Item decode_single(const Params& p, int li) {
   Item it;
+  it.chunk = p.chunk;
   it.b = 0;
   it.si.off = 0;
   it.si.T = p.total_nodes;
@@ -674,8 +732,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
   int my_id = -1;
   {
-    const int lb = it.s * (p.chunk / kBlock) + lane;
-    if (lane < p.chunk / kBlock && lb < p.max_blocks)
+    const int lb = it.s * (it.chunk / kBlock) + lane;
+    if (lane < it.chunk / kBlock && lb < p.max_blocks)
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
   wait_vm<0>();
@@ -688,11 +746,11 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     const bool p_ok = p_read >= 0 && p_read <= p.max_prefix;
     if (!p_ok && tid == 0 && first_of_launch) set_error(p.hdr, kErrBadPrefix);
     si.P = p_ok ? p_read : 0;
-    si.S = si.P > 0 ? cdiv(si.P, p.chunk) : 1;
+    si.S = si.P > 0 ? cdiv(si.P, it.chunk) : 1;
     if (it.s >= si.S) return;  // a chunk past the actual prefix
   }
-  const int t0 = it.s * p.chunk;
-  const int ntok = max(0, min(si.P, t0 + p.chunk) - t0);
+  const int t0 = it.s * it.chunk;
+  const int ntok = max(0, min(si.P, t0 + it.chunk) - t0);
   const int nblk = cdiv(ntok, kBlock);
   const int S = si.S;
   const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
@@ -1243,10 +1301,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   const int tid = threadIdx.x;
 
   int items;
+  int chunk = p.chunk;
   if (p.single) {
     items = p.single_items;  // the tree offsets are checked by the launch's first item
   } else {
-    items = build_table(p, cum, ot, pl, perm, sm.scratch);
+    items = build_table(p, cum, ot, pl, perm, sm.scratch, chunk);
   }
 
   // items in increasing order: first blockIdx.x, then from the ticket counter.
@@ -1256,7 +1315,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   int li = int(blockIdx.x);
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
-    const Item it = p.single ? decode_single(p, li) : decode_item(p, cum, ot, pl, perm, li);
+    const Item it = p.single ? decode_single(p, li) : decode_item(p, chunk, cum, ot, pl, perm, li);
     process_item<T, D, FUSED>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
