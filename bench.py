@@ -446,6 +446,9 @@ def main() -> int:
             "prefix_tokens": int(inp.prefix_lens.sum()),
             "tree_nodes": inp.total_tree_nodes,
             "split_tokens": split,
+            "chunk_rule": ("host" if args.split_tokens > 0 or inp.batch == 1 else
+                           "device: from the actual prefix lengths when the groups are fewer "
+                           "than the workgroups, else split_tokens"),
             "replicas": R,
             "algorithmic_bytes": nbytes,
             "algorithmic_flops": flops,
