@@ -20,7 +20,7 @@ against hand-derived tables, closed forms, a library attention routine and
 invariants.  Numeric values at the five synthetic configs themselves are pinned
 only through those invariants (the pages print no output values).
 """
-from .commit import accept_greedy, commit  # noqa: F401
+from .commit import accept_greedy, commit, commit_incache  # noqa: F401
 from .tree_attention import (  # noqa: F401
     ancestor_or_self_mask,
     build_masks,
@@ -28,7 +28,9 @@ from .tree_attention import (  # noqa: F401
     prefix_only,
     suffix_only,
     to_f64,
+    tree_rows_from_cache,
     verify,
+    verify_incache,
     verify_rows,
     visibility,
 )

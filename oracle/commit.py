@@ -161,3 +161,49 @@ def commit(inp, accept_len, path, free_blocks, free_count: int) -> Dict[str, obj
         plen[b] = P + int(accept_len[b])
     return dict(k_cache=k_cache, v_cache=v_cache, block_table=table, prefix_lens=plen,
                 blocks_taken=nxt, error=error)
+
+
+def commit_incache(inp, accept_len, path) -> Dict[str, object]:
+    """Commit for the in-cache layout: the tree's rows already sit at cache
+    positions P .. P+T-1 of each sequence, so the accepted path is compacted
+    in place -- position P + t takes the row that was at P + path[t] before
+    the commit -- and the prefix length grows by the path length.  Rows past
+    the new prefix are left as they are (no longer part of the history).  A
+    path that is not a root path skips its sequence (``"bad_tree"``); so does
+    a tree region that runs past the sequence's table row (``"bad_prefix"``).
+    [pith.science verdict record: paged KV with tree padding; fdeinterviews.com
+    summary: the cache must hold exactly the committed history]
+    """
+    B = inp.batch
+    k_cache = inp.k_cache.copy()
+    v_cache = inp.v_cache.copy()
+    plen = inp.prefix_lens.copy()
+    maxb = inp.block_table.shape[1]
+    error = 0
+    for b in range(B):
+        lo, hi = int(inp.tree_offsets[b]), int(inp.tree_offsets[b + 1])
+        par = inp.parents[lo:hi]
+        T = hi - lo
+        A = int(accept_len[b])
+        good = 0 <= A <= T
+        for t in range(A if good else 0):
+            node = int(path[b, t])
+            want_parent = -1 if t == 0 else int(path[b, t - 1])
+            if not (0 <= node < T and int(par[node]) == want_parent):
+                good = False
+                break
+        if not good:
+            error = error or "bad_tree"
+            continue
+        P = int(plen[b])
+        if not (0 <= P and P + T <= BLOCK * maxb):
+            error = error or "bad_prefix"
+            continue
+        for t in range(A):
+            src, dst = P + int(path[b, t]), P + t
+            sb, db = int(inp.block_table[b, src // BLOCK]), int(inp.block_table[b, dst // BLOCK])
+            k_cache[db, :, dst % BLOCK, :] = inp.k_cache[sb, :, src % BLOCK, :]
+            v_cache[db, :, dst % BLOCK, :] = inp.v_cache[sb, :, src % BLOCK, :]
+        plen[b] = P + A
+    return dict(k_cache=k_cache, v_cache=v_cache, prefix_lens=plen, error=error)
+

@@ -192,6 +192,40 @@ def verify(inp) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return o, lse, build_masks(inp)
 
 
+def tree_rows_from_cache(inp) -> Tuple[np.ndarray, np.ndarray]:
+    """The tree K/V rows of an in-cache batch: node i of sequence b is cache
+    position prefix_lens[b] + i, read through the block table (slot
+    (P + i) % 64 of block block_table[b][(P + i) // 64]).  Returns
+    (k_tree, v_tree) [N, Hkv, D] in the storage dtype (a plain gather).
+    [pith.science verdict record: paged KV with tree padding, and
+    paged/persistent KV-cache handling for tree attention]"""
+    N = inp.total_tree_nodes
+    kt = np.empty((N,) + inp.k_cache.shape[1:2] + inp.k_cache.shape[3:], dtype=inp.k_cache.dtype)
+    vt = np.empty_like(kt)
+    bs = inp.block_size
+    for b in range(inp.batch):
+        lo, hi = int(inp.tree_offsets[b]), int(inp.tree_offsets[b + 1])
+        P = int(inp.prefix_lens[b])
+        for i in range(hi - lo):
+            pos = P + i
+            blk = int(inp.block_table[b, pos // bs])
+            kt[lo + i] = inp.k_cache[blk, :, pos % bs, :]
+            vt[lo + i] = inp.v_cache[blk, :, pos % bs, :]
+    return kt, vt
+
+
+def verify_incache(inp) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """:func:`verify` for a batch whose tree K/V rows sit in the paged cache
+    right after each prefix (``inp.k_tree`` / ``inp.v_tree`` are ignored):
+    the rows are gathered (:func:`tree_rows_from_cache`) and the definition
+    is the same.  The prefix piece still covers positions [0, P) only."""
+    import copy
+    kt, vt = tree_rows_from_cache(inp)
+    view = copy.copy(inp)
+    view.k_tree, view.v_tree = kt, vt
+    return verify(view)
+
+
 def verify_rows(inp, rows) -> Tuple[np.ndarray, np.ndarray]:
     """Same definition as :func:`verify`, evaluated only for the listed
     (node row n, query head h) pairs.  Returns (o [k, D], lse [k])."""

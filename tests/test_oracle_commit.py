@@ -210,3 +210,73 @@ def test_commit_nothing_when_table_row_full():
     r = oracle.commit(inp, n, path, free, len(free))
     assert r["error"] == "no_blocks"
     assert np.array_equal(r["prefix_lens"], inp.prefix_lens)
+
+
+# ------------------------------------------------------- in-cache tree rows
+def test_incache_verify_equals_separate_tree_rows():
+    from workloads import place_tree_in_cache
+    rng = np.random.default_rng(31)
+    inp = make_inputs(dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                      prefix_lens=[63, 0, 130], trees=[TREE_12, TREE_CHAIN4, TREE_12], rng=rng,
+                      spare_blocks=6, extra_table_cols=1)
+    ic, _ = place_tree_in_cache(inp, rng)
+    # the gathered rows are the tree rows, bit for bit
+    kt, vt = oracle.tree_rows_from_cache(ic)
+    assert np.array_equal(kt.view(np.uint16), inp.k_tree.view(np.uint16))
+    assert np.array_equal(vt.view(np.uint16), inp.v_tree.view(np.uint16))
+    # so the verify outputs agree exactly; the prefix piece still ends at P
+    o1, l1, _ = oracle.verify(inp)
+    ic.k_tree = np.zeros_like(inp.k_tree)          # must not be read
+    o2, l2, _ = oracle.verify_incache(ic)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_incache_commit_matches_separate_commit_and_attention():
+    from workloads import place_tree_in_cache
+    rng = np.random.default_rng(32)
+    inp = make_inputs(dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                      prefix_lens=[63, 5, 190], trees=[TREE_12, TREE_CHAIN4, TREE_12], rng=rng,
+                      spare_blocks=8, extra_table_cols=1)
+    draft, argmax = make_tokens(inp.parents, inp.tree_offsets, rng, p_match=0.8, vocab=30)
+    n, path, _ = oracle.accept_greedy(inp.parents, inp.tree_offsets, draft, argmax, 12)
+    ic, _ = place_tree_in_cache(inp, rng)
+    o_ver, l_ver, _ = oracle.verify_incache(ic)
+    r = oracle.commit_incache(ic, n, path)
+    assert r["error"] == 0
+    for b in range(inp.batch):
+        P, A = int(inp.prefix_lens[b]), int(n[b])
+        assert r["prefix_lens"][b] == P + A
+        lo = int(inp.tree_offsets[b])
+        got = _gather(r["k_cache"], ic.block_table[b], P + A)
+        # the committed history: the old prefix, then the accepted rows in path order
+        assert np.array_equal(got[:P], _gather(inp.k_cache, inp.block_table[b], P))
+        assert np.array_equal(got[P:], inp.k_tree[lo + path[b, :A]])
+        # and the last accepted node sees exactly that history
+        last = lo + int(path[b, n[b] - 1])
+        one = make_inputs(dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                          prefix_lens=[0], trees=[[-1]], rng=np.random.default_rng(0))
+        one.k_cache, one.v_cache = r["k_cache"], r["v_cache"]
+        one.block_table = ic.block_table[b:b + 1]
+        one.prefix_lens = r["prefix_lens"][b:b + 1].copy()
+        one.q = inp.q[last:last + 1]
+        o_pre, l_pre = oracle.prefix_only(one)
+        assert np.allclose(o_pre[0], o_ver[last], atol=1e-12, rtol=0)
+        assert np.allclose(l_pre[0], l_ver[last], atol=1e-12, rtol=0)
+
+
+def test_incache_commit_bad_path_skips_sequence():
+    from workloads import place_tree_in_cache
+    rng = np.random.default_rng(33)
+    inp = make_inputs(dtype="bf16", num_q_heads=2, num_kv_heads=1, head_dim=64,
+                      prefix_lens=[10, 70], trees=[TREE_12, TREE_12], rng=rng,
+                      spare_blocks=4, extra_table_cols=1)
+    draft, argmax = make_tokens(inp.parents, inp.tree_offsets, rng, p_match=1.0, vocab=30)
+    n, path, _ = oracle.accept_greedy(inp.parents, inp.tree_offsets, draft, argmax, 12)
+    ic, _ = place_tree_in_cache(inp, rng)
+    bad = path.copy()
+    bad[1, 1] = 2 if bad[1, 1] != 2 else 3
+    bad[1, 2] = 4 if bad[1, 1] != 1 else 5   # 4 and 5 are children of 1 only
+    r = oracle.commit_incache(ic, n, bad)
+    assert r["error"] == "bad_tree"
+    assert r["prefix_lens"][1] == inp.prefix_lens[1]
+    assert r["prefix_lens"][0] == inp.prefix_lens[0] + n[0]

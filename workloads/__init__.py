@@ -4,7 +4,7 @@ This package only draws random numbers and lays them out in memory.  It holds
 none of the attention arithmetic: the fp64 oracle and the HIP library both
 consume what it produces, and neither imports the other.
 """
-from .commit import free_list, make_tokens  # noqa: F401
+from .commit import free_list, make_tokens, place_tree_in_cache  # noqa: F401
 from .configs import (  # noqa: F401
     CONFIG_NAMES,
     TREE_12,

@@ -17,6 +17,10 @@ Recipe (the pages give no token statistics; these are plain readings):
 * Commit state: the verify batch is built with spare pool blocks and extra
   block-table columns; the free list is a seeded permutation of the pool
   blocks no sequence uses.
+* In-cache layout ("tree padding"): each sequence's tree rows are written
+  into its cache positions P .. P+T-1; blocks the region needs beyond the
+  prefix's come from the free list in batch order.  The tree K/V arrays keep
+  the same rows.
 """
 from __future__ import annotations
 
@@ -62,3 +66,31 @@ def free_list(inp, rng: np.random.Generator) -> np.ndarray:
     used[t[t >= 0]] = True
     free = np.nonzero(~used)[0]
     return rng.permutation(free).astype(np.int32)
+
+
+def place_tree_in_cache(inp, rng: np.random.Generator):
+    """A copy of ``inp`` whose tree K/V rows also sit in the paged cache right
+    after each prefix (positions P .. P+T-1), with the table rows extended as
+    needed; returns (new inputs, free blocks left)."""
+    import copy
+    out = copy.copy(inp)
+    out.k_cache = inp.k_cache.copy()
+    out.v_cache = inp.v_cache.copy()
+    out.block_table = inp.block_table.copy()
+    free = list(free_list(inp, rng))
+    for b in range(inp.batch):
+        lo, hi = int(inp.tree_offsets[b]), int(inp.tree_offsets[b + 1])
+        P = int(inp.prefix_lens[b])
+        have = -(-P // 64)
+        after = -(-(P + hi - lo) // 64)
+        if after > out.block_table.shape[1]:
+            raise ValueError(f"sequence {b}: table row too short for the tree region")
+        for k in range(have, after):
+            out.block_table[b, k] = free.pop(0)
+        for i in range(hi - lo):
+            pos = P + i
+            blk = out.block_table[b, pos // 64]
+            out.k_cache[blk, :, pos % 64, :] = inp.k_tree[lo + i]
+            out.v_cache[blk, :, pos % 64, :] = inp.v_tree[lo + i]
+    return out, np.asarray(free, dtype=np.int32)
+
