@@ -171,6 +171,40 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
                            const int32_t* tree_offsets, void* out, float* lse_out,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Fused verify for the in-cache tree layout ("tree padding"): the tree K/V
+ * rows of sequence b are not separate tensors but sit in the paged cache right
+ * after its prefix, node i at position prefix_lens[b] + i (slot (P+i) % 64 of
+ * block block_table[b][(P+i)/64]).  The prefix piece covers positions
+ * [0, P) as in tree_attn_verify; the tree piece reads its rows through the
+ * block table, so the tree K/V need no separate write.  Each table row must
+ * cover P + T positions; a region block id outside [0, num_blocks) or a row
+ * too short raises TA_ERR_BAD_PREFIX.  Same shape, workspace and outputs as
+ * tree_attn_verify.  [pith.science verdict record: desk editor letter (paged
+ * KV with tree padding) and referee summary (paged/persistent KV-cache
+ * handling for tree attention)] */
+ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* prefix_lens, const int32_t* parents,
+                                   const int32_t* tree_offsets, void* out, float* lse_out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Commit for the in-cache layout: the accepted path (root first, as
+ * tree_attn_accept_greedy writes it) is compacted in place -- position P + t
+ * takes the row that was at P + accept_path[b][t], for every KV head -- and
+ * prefix_lens[b] becomes P + accept_len[b].  No block is allocated (the tree
+ * region's blocks are already in the table); rows past the new prefix are
+ * left as they are and are no longer history.  A path that is not a root
+ * path: TA_ERR_BAD_TREE; a region running past the table row or a region
+ * block id out of range: TA_ERR_BAD_PREFIX; either way that sequence is left
+ * as it was.  One kernel launch, one workgroup per sequence.  Only the
+ * workspace header is used.  [same sources; fdeinterviews.com summary,
+ * paragraph on hidden correctness obligations] */
+ta_status tree_attn_commit_incache(const ta_shape* shape, const int32_t* parents,
+                                   const int32_t* tree_offsets, const int32_t* accept_len,
+                                   const int32_t* accept_path, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, int32_t* prefix_lens, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
 /* Greedy acceptance after verification, one sequence per wave.  For tree
  * node i of sequence b (local index), draft_tokens[i] is the token the node
  * stands for and target_argmax[i] the target model's greedy next token at it

@@ -213,6 +213,52 @@ def verify(shape: Shape, q, k_cache, v_cache, block_table, prefix_lens, k_tree, 
     return out, lse
 
 
+def verify_incache(shape: Shape, q, k_cache, v_cache, block_table, prefix_lens, parents,
+                   tree_offsets, workspace, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused verify with the tree K/V rows in the paged cache right after each
+    prefix (tree_attn_verify_incache)."""
+    _check_prefix_inputs(shape, q, k_cache, v_cache, block_table, prefix_lens, tree_offsets)
+    N, Hq, D = shape.total_tree_nodes, shape.num_q_heads, shape.head_dim
+    el = _elem(shape)
+    _want(parents, "parents", torch.int32, (N,))
+    if out is None:
+        out = torch.empty(N, Hq, D, dtype=el, device=q.device)
+    _want(out, "out", el, (N, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty(N, Hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _want(lse, "lse_out", torch.float32, (N, Hq))
+    _check(load().tree_attn_verify_incache(ctypes.byref(shape), _ptr(q), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(block_table), _ptr(prefix_lens),
+                                           _ptr(parents), _ptr(tree_offsets), _ptr(out), _ptr(lse),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tree_attn_verify_incache")
+    return out, lse
+
+
+def commit_incache(shape: Shape, parents, tree_offsets, accept_len, accept_path, k_cache,
+                   v_cache, block_table, prefix_lens, workspace, stream=None) -> None:
+    """Compact the accepted paths in place in the in-cache layout and advance
+    prefix_lens (tree_attn_commit_incache)."""
+    N, B, Hkv, D = (shape.total_tree_nodes, shape.batch, shape.num_kv_heads, shape.head_dim)
+    el = _elem(shape)
+    _want(parents, "parents", torch.int32, (N,))
+    _want(tree_offsets, "tree_offsets", torch.int32, (B + 1,))
+    _want(accept_len, "accept_len", torch.int32, (B,))
+    _want(accept_path, "accept_path", torch.int32, (B, shape.max_tree_nodes))
+    _want(k_cache, "k_cache", el, (shape.num_blocks, Hkv, 64, D))
+    _want(v_cache, "v_cache", el, (shape.num_blocks, Hkv, 64, D))
+    _want(block_table, "block_table", torch.int32, (B, shape.max_blocks_per_seq))
+    _want(prefix_lens, "prefix_lens", torch.int32, (B,))
+    _check(load().tree_attn_commit_incache(ctypes.byref(shape), _ptr(parents), _ptr(tree_offsets),
+                                           _ptr(accept_len), _ptr(accept_path), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(block_table), _ptr(prefix_lens),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tree_attn_commit_incache")
+
+
 def accept_greedy(shape: Shape, parents, tree_offsets, draft_tokens, target_argmax, workspace,
                   stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Greedy path acceptance (tree_attn_accept_greedy): returns accept_len [B],

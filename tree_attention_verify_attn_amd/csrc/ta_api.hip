@@ -453,6 +453,72 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
   return static_cast<ta_status>(dispatch_attn<true>(shape, p, L, stream));
 }
 
+ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* prefix_lens, const int32_t* parents,
+                                   const int32_t* tree_offsets, void* out, float* lse_out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!prefix_lens || !tree_offsets || !block_table || !k_cache || !v_cache)
+    return TA_ERR_INVALID_ARG;
+  if (shape->num_blocks < 1) return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && (!q || !parents || !out)) return TA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return TA_ERR_INVALID_ARG;
+  WsLayout L = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true));
+  st = check_ws(shape, L, ws, ws_bytes);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->total_tree_nodes == 0) return TA_OK;
+  Params p = base_params(shape, L, ws);
+  p.single = 0;  // the tree rows' block ids need P before the item's first trip
+  p.tree_in_cache = 1;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.prefix_lens = prefix_lens;
+  p.parents = parents;
+  p.tree_offsets = tree_offsets;
+  p.out = out;
+  p.lse_out = lse_out;
+  return static_cast<ta_status>(dispatch_attn<true>(shape, p, L, stream));
+}
+
+ta_status tree_attn_commit_incache(const ta_shape* shape, const int32_t* parents,
+                                   const int32_t* tree_offsets, const int32_t* accept_len,
+                                   const int32_t* accept_path, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, int32_t* prefix_lens, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens ||
+      !k_cache || !v_cache)
+    return TA_ERR_INVALID_ARG;
+  if (shape->total_tree_nodes > 0 && !parents) return TA_ERR_INVALID_ARG;
+  if (shape->num_blocks < 1 || !aligned16(k_cache) || !aligned16(v_cache)) return TA_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < sizeof(WsHeader)) return TA_ERR_WORKSPACE;
+  IncacheParams c{};
+  c.parents = parents;
+  c.tree_offsets = tree_offsets;
+  c.accept_len = accept_len;
+  c.path = accept_path;
+  c.k_cache = k_cache;
+  c.v_cache = v_cache;
+  c.block_table = block_table;
+  c.prefix_lens = prefix_lens;
+  c.hdr = static_cast<WsHeader*>(ws);
+  c.batch = shape->batch;
+  c.total_nodes = shape->total_tree_nodes;
+  c.max_tree = shape->max_tree_nodes;
+  c.max_blocks = shape->max_blocks_per_seq;
+  c.num_blocks = shape->num_blocks;
+  c.hkv = shape->num_kv_heads;
+  c.row_bytes = shape->head_dim * (shape->dtype == TA_DTYPE_BF16 ? 2 : 4);
+  hipLaunchKernelGGL(commit_incache_kernel, dim3(unsigned(shape->batch)), dim3(kThreads), 0,
+                     stream, c);
+  return static_cast<ta_status>(launch_status());
+}
+
 ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
                                   const int32_t* tree_offsets, const int32_t* draft_tokens,
                                   const int32_t* target_argmax, int32_t* accept_len,

@@ -238,4 +238,109 @@ __global__ void __launch_bounds__(kThreads) commit_apply_kernel(CommitParams c) 
   }
 }
 
+// ------------------------------------------------- commit, in-cache layout
+// The tree's rows already sit at cache positions P .. P+T-1 (the "tree
+// padding" layout: paged KV with the tree after the prefix, pith.science
+// verdict record, desk editor letter).  One workgroup per sequence: wave 0
+// checks the path and the region's (at most two) block ids; then the
+// accepted rows are compacted in place -- position P + t takes the row at
+// P + path[t] -- in rounds of 8 x 16 bytes per thread, all loads of a round
+// before any of its stores.  Row chunks are numbered t-major and path[t] >= t
+// (a root path climbs in index), so a chunk's source is never overwritten by
+// an earlier round.  The prefix length then grows by the path length.
+struct IncacheParams {
+  const int32_t* parents;
+  const int32_t* tree_offsets;
+  const int32_t* accept_len;
+  const int32_t* path;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  int32_t* prefix_lens;
+  WsHeader* hdr;
+  int batch, total_nodes, max_tree, max_blocks, num_blocks, hkv, row_bytes;
+};
+
+__global__ void __launch_bounds__(kThreads) commit_incache_kernel(IncacheParams c) {
+  __shared__ int sh[5];  // ok, P, A, first block, second block
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  if (tid < 64) {
+    const int o0 = c.tree_offsets[b];
+    const int o1 = c.tree_offsets[b + 1];
+    const int T = o1 - o0;
+    const int A = c.accept_len[b];
+    const int P = c.prefix_lens[b];
+    bool ok = o0 >= 0 && o1 > o0 && o1 <= c.total_nodes && T <= c.max_tree && A >= 0 && A <= T;
+    const bool mine = ok && lane < A;
+    const int node = mine ? c.path[size_t(b) * c.max_tree + lane] : -1;
+    const int prev = __shfl_up(node, 1);
+    bool step_ok = true;
+    if (mine) step_ok = node >= 0 && node < T && c.parents[o0 + node] == (lane == 0 ? -1 : prev);
+    ok = ok && __all(step_ok);
+    const bool p_ok = P >= 0 && P + T <= kBlock * c.max_blocks;
+    int blk = 0;
+    if (p_ok && lane < 2 && P / kBlock + lane < c.max_blocks)
+      blk = c.block_table[size_t(b) * c.max_blocks + P / kBlock + lane];
+    const int blk0 = __shfl(blk, 0);
+    const int blk1 = __shfl(blk, 1);
+    const bool two = p_ok && (P + T - 1) / kBlock > P / kBlock;
+    const bool blk_ok = p_ok && blk0 >= 0 && blk0 < c.num_blocks &&
+                        (!two || (blk1 >= 0 && blk1 < c.num_blocks));
+    if (lane == 0) {
+      if (!ok) set_error(c.hdr, kErrBadTree);
+      else if (!blk_ok) set_error(c.hdr, kErrBadPrefix);
+      sh[0] = ok && blk_ok;
+      sh[1] = P;
+      sh[2] = A;
+      sh[3] = blk0;
+      sh[4] = blk1;
+    }
+  }
+  __syncthreads();
+  if (!sh[0]) return;
+  const int P = sh[1], A = sh[2], blk0 = sh[3], blk1 = sh[4];
+  const int chunks = c.row_bytes / 16;
+  const int per_t = c.hkv * chunks;
+  const int total = A * per_t;
+  constexpr int kPer = 8;
+  unsigned char* kc = static_cast<unsigned char*>(c.k_cache);
+  unsigned char* vc = static_cast<unsigned char*>(c.v_cache);
+  auto addr = [&](int pos, int g, int ch) {
+    const int blk = pos / kBlock == P / kBlock ? blk0 : blk1;
+    return ((size_t(blk) * c.hkv + g) * kBlock + pos % kBlock) * c.row_bytes + size_t(ch) * 16;
+  };
+  for (int base = 0; base < total; base += kThreads * kPer) {
+    uint4 kr[kPer], vr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = base + i * kThreads + tid;
+      if (u < total) {
+        const int t = u / per_t;
+        const int g = (u % per_t) / chunks;
+        const int ch = u % chunks;
+        const size_t a = addr(P + c.path[size_t(b) * c.max_tree + t], g, ch);
+        kr[i] = *reinterpret_cast<const uint4*>(kc + a);
+        vr[i] = *reinterpret_cast<const uint4*>(vc + a);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = base + i * kThreads + tid;
+      if (u < total) {
+        const int t = u / per_t;
+        const int g = (u % per_t) / chunks;
+        const int ch = u % chunks;
+        const size_t a = addr(P + t, g, ch);
+        *reinterpret_cast<uint4*>(kc + a) = kr[i];
+        *reinterpret_cast<uint4*>(vc + a) = vr[i];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) c.prefix_lens[b] = P + A;
+}
+
 }  // namespace ta

@@ -84,6 +84,7 @@ struct Params {
   int s_max;                 // chunks per group, upper bound
   int item_slots;            // num_groups * s_max: bound on item numbers
   int chunk_auto;            // 1: the kernel may pick the chunk from the actual prefix lengths
+  int tree_in_cache;         // 1: tree K/V rows are cache positions P .. P+T-1 (k_tree unused)
   int single;                // 1: one sequence, items numbered without a table
   int single_items;          // item count of a one-sequence launch
   int first_round;           // workgroups in the grid

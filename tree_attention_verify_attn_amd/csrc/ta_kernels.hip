@@ -722,6 +722,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // chunk that is is known only with the prefix length, so every chunk reads it)
   int par = -1;
   if (FUSED && w == 0 && (need_p || it.s == si.S - 1)) par = p.parents[si.off + min(lane, si.T - 1)];
+  // tree rows kept in the cache right after the prefix (positions P .. P+T-1,
+  // at most two blocks): lanes 0 and 1 of every wave read those blocks' ids.
+  // Such launches always use the sequence table, so P is known here.
+  int tree_blk = 0;
+  const bool tree_here = FUSED && p.tree_in_cache && it.s == si.S - 1;
+  if (tree_here && lane < 2)
+    tree_blk = hidden_load(p.block_table + size_t(it.b) * p.max_blocks +
+                           min(si.P / kBlock + lane, p.max_blocks - 1));
   // one-sequence numbering: the prefix length, and (first item only) the two
   // tree offsets, which must be 0 and N
   const bool first_of_launch = it.s == 0 && it.g == 0 && it.rp == 0;
@@ -738,6 +746,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
   wait_vm<0>();
   const unsigned sense0 = unsigned(settle(sense_read));
+  tree_blk = settle(tree_blk);
   if (need_p) {
     p_read = __builtin_amdgcn_readfirstlane(settle(p_read));  // the same in every lane
     toff = settle(toff);
@@ -765,14 +774,42 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   if (with_tree) {
     const int Tn = si.T;
     const int ninstr = p.tree_lds_half / 1024;
+    // in-cache rows: the region's two block ids (checked; a bad one is
+    // flagged and read as block 0)
+    int blk0 = 0, blk1 = 0;
+    if (p.tree_in_cache) {
+      blk0 = __shfl(tree_blk, 0);
+      blk1 = __shfl(tree_blk, 1);
+      const int last_idx = (si.P + Tn - 1) / kBlock;
+      const bool two = last_idx > si.P / kBlock;
+      const bool ok = last_idx < p.max_blocks && blk0 >= 0 && blk0 < p.num_blocks &&
+                      (!two || (blk1 >= 0 && blk1 < p.num_blocks));
+      if (!ok) {
+        if (tid == 0) set_error(p.hdr, kErrBadPrefix);
+        blk0 = blk1 = 0;
+      }
+    }
     for (int m = w; m < ninstr; m += kAttnWaves) {
       const int u = m * 64 + lane;
       const int t = min(u / KCH, Tn - 1);
       const int pc = u % KCH;
       const int c = pc ^ ((u / KCH) & SWZ);
-      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
-      const unsigned char* gk = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff);
-      const unsigned char* gv = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff);
+      size_t roff;
+      const T* kb;
+      const T* vb;
+      if (p.tree_in_cache) {
+        const int pos = si.P + t;
+        const int blk = (pos / kBlock == si.P / kBlock) ? blk0 : blk1;
+        roff = ((size_t(blk) * p.hkv + it.g) * kBlock + (pos % kBlock)) * D;
+        kb = static_cast<const T*>(p.k_cache);
+        vb = static_cast<const T*>(p.v_cache);
+      } else {
+        roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+        kb = static_cast<const T*>(p.k_tree);
+        vb = static_cast<const T*>(p.v_tree);
+      }
+      const unsigned char* gk = reinterpret_cast<const unsigned char*>(kb + roff);
+      const unsigned char* gv = reinterpret_cast<const unsigned char*>(vb + roff);
       lds_dma16(gk + c * 16, tk + m * 1024);
       lds_dma16(gv + c * 16, tv + m * 1024);
     }

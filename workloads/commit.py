@@ -86,7 +86,8 @@ def place_tree_in_cache(inp, rng: np.random.Generator):
         if after > out.block_table.shape[1]:
             raise ValueError(f"sequence {b}: table row too short for the tree region")
         for k in range(have, after):
-            out.block_table[b, k] = free.pop(0)
+            if out.block_table[b, k] < 0:     # a region block the row does not hold yet
+                out.block_table[b, k] = free.pop(0)
         for i in range(hi - lo):
             pos = P + i
             blk = out.block_table[b, pos // 64]
