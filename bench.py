@@ -145,6 +145,27 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
     }
 
 
+def incache_layout(inp):
+    """The same batch with each tree's K/V rows also written into the paged
+    cache right after its prefix (two spare blocks and table columns per
+    sequence are added for the region); input preparation only."""
+    import copy
+
+    import numpy as np
+
+    from workloads import place_tree_in_cache
+    B = inp.batch
+    nan = np.uint16(0x7FC0) if inp.dtype == "bf16" else np.float32(np.nan)
+    pad = np.full((2 * B,) + inp.k_cache.shape[1:], nan, dtype=inp.k_cache.dtype)
+    ext = copy.copy(inp)
+    ext.k_cache = np.concatenate([inp.k_cache, pad])
+    ext.v_cache = np.concatenate([inp.v_cache, pad])
+    ext.block_table = np.concatenate(
+        [inp.block_table, np.full((B, 2), -1, dtype=np.int32)], axis=1)
+    ic, _ = place_tree_in_cache(ext, np.random.default_rng(inp.seed + 7))
+    return ic
+
+
 def bench_after_verify(ta, torch, np, steps: int) -> dict:
     """Greedy acceptance and commit timed on a 256-sequence batch with the
     ragged workload's tree mix (1-node / chain-4 / 12-node at 0.2/0.5/0.3),
@@ -260,8 +281,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
-    ap.add_argument("--entry", choices=("verify", "split"), default="verify",
-                    help="fused single launch (default) or the four-call split path")
+    ap.add_argument("--entry", choices=("verify", "split", "incache"), default="verify",
+                    help="fused single launch (default), the four-call split path, or the fused "
+                         "launch with the tree rows kept in the paged cache after each prefix")
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,6 +326,8 @@ def main() -> int:
 
     log(f"building workload cfg{args.config}")
     inp = make_config(args.config)
+    if args.entry == "incache":
+        inp = incache_layout(inp)
     nbytes = algorithmic_bytes(inp)
     flops = algorithmic_flops(inp)
     dt = ta.DTYPE_BF16 if inp.dtype == "bf16" else ta.DTYPE_F32
@@ -347,7 +371,15 @@ def main() -> int:
                           lses[r].data_ptr(), wsp, wsn, sh))
     verify = lib.tree_attn_verify
 
-    if args.entry == "verify":
+    if args.entry == "incache":
+        verify_ic = lib.tree_attn_verify_incache
+
+        def step(r):
+            a = call_args[r]
+            rc = verify_ic(*a[:6], *a[8:])    # no separate tree K/V tensors
+            if rc:
+                raise RuntimeError(f"tree_attn_verify_incache: {ta.status_string(rc)}")
+    elif args.entry == "verify":
         def step(r):
             rc = verify(*call_args[r])
             if rc:
@@ -419,7 +451,7 @@ def main() -> int:
         raise RuntimeError(f"device error during timing: {ta.status_string(err)}")
 
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.config, split)
+    traffic = measured_traffic(args.config, split) if args.entry == "verify" else None
     result = {
         "metric": METRIC,
         "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -461,7 +493,9 @@ def main() -> int:
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "kernel": (f"attn_kernel<{'bf16' if inp.dtype == 'bf16' else 'f32'},{D},fused> "
-                       "(tree_attn_verify)" if args.entry == "verify"
+                       + ("(tree_attn_verify)" if args.entry == "verify"
+                          else "(tree_attn_verify_incache)")
+                       if args.entry in ("verify", "incache")
                        else "split path: mask + prefix + suffix + merge kernels"),
             "mfma_util": round(flops / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
         },

@@ -470,7 +470,9 @@ ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const v
   if (st != kOk) return static_cast<ta_status>(st);
   if (shape->total_tree_nodes == 0) return TA_OK;
   Params p = base_params(shape, L, ws);
-  p.single = 0;  // the tree rows' block ids need P before the item's first trip
+  // one-sequence numbering needs spare lanes in the block-id load for the tree
+  // region's blocks (the region's position is known only with P)
+  if (L.chunk / kBlock + 2 > 64) p.single = 0;
   p.tree_in_cache = 1;
   p.q = q;
   p.k_cache = k_cache;

@@ -723,11 +723,16 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   int par = -1;
   if (FUSED && w == 0 && (need_p || it.s == si.S - 1)) par = p.parents[si.off + min(lane, si.T - 1)];
   // tree rows kept in the cache right after the prefix (positions P .. P+T-1,
-  // at most two blocks): lanes 0 and 1 of every wave read those blocks' ids.
-  // Such launches always use the sequence table, so P is known here.
+  // at most two blocks).  The region starts inside this chunk's block range
+  // or right after it, so two more lanes of the block-id load below cover its
+  // blocks (lanes cpb and cpb + 1 of the id vector), also before P is known.
+  // When a chunk spans 63 or 64 blocks there are no spare lanes: lanes 0 and
+  // 1 of every wave then read the two ids (such launches use the sequence
+  // table, so P is known here).
+  const int cpb = it.chunk / kBlock;  // blocks per chunk
+  const bool extra_lanes = FUSED && p.tree_in_cache && cpb + 2 <= 64;
   int tree_blk = 0;
-  const bool tree_here = FUSED && p.tree_in_cache && it.s == si.S - 1;
-  if (tree_here && lane < 2)
+  if (FUSED && p.tree_in_cache && !extra_lanes && it.s == si.S - 1 && lane < 2)
     tree_blk = hidden_load(p.block_table + size_t(it.b) * p.max_blocks +
                            min(si.P / kBlock + lane, p.max_blocks - 1));
   // one-sequence numbering: the prefix length, and (first item only) the two
@@ -740,8 +745,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
   int my_id = -1;
   {
-    const int lb = it.s * (it.chunk / kBlock) + lane;
-    if (lane < it.chunk / kBlock && lb < p.max_blocks)
+    const int lb = it.s * cpb + lane;
+    if (lane < cpb + (extra_lanes ? 2 : 0) && lb < p.max_blocks)
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
   wait_vm<0>();
@@ -778,8 +783,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     // flagged and read as block 0)
     int blk0 = 0, blk1 = 0;
     if (p.tree_in_cache) {
-      blk0 = __shfl(tree_blk, 0);
-      blk1 = __shfl(tree_blk, 1);
+      if (extra_lanes) {
+        const int r0 = si.P / kBlock - it.s * cpb;  // 0 .. cpb
+        blk0 = __shfl(my_id, r0);
+        blk1 = __shfl(my_id, r0 + 1);
+      } else {
+        blk0 = __shfl(tree_blk, 0);
+        blk1 = __shfl(tree_blk, 1);
+      }
       const int last_idx = (si.P + Tn - 1) / kBlock;
       const bool two = last_idx > si.P / kBlock;
       const bool ok = last_idx < p.max_blocks && blk0 >= 0 && blk0 < p.num_blocks &&
