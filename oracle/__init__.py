@@ -23,7 +23,9 @@ only through those invariants (the pages print no output values).
 from .commit import accept_greedy, commit, commit_incache  # noqa: F401
 from .tree_attention import (  # noqa: F401
     ancestor_or_self_mask,
+    ancestor_or_self_words,
     build_masks,
+    build_masks_words,
     merge,
     prefix_only,
     suffix_only,

@@ -90,6 +90,31 @@ def ancestor_or_self_mask(parents) -> np.ndarray:
     return out
 
 
+def ancestor_or_self_words(parents, words: int) -> np.ndarray:
+    """uint64 [T, words]: bit j % 64 of word j // 64 in row i is set iff j is i
+    or an ancestor of i -- the same mask for trees of more than 64 nodes,
+    spread over several 64-bit words (T <= 64 * words)."""
+    vis = visibility(parents)
+    T = vis.shape[0]
+    if T > 64 * words:
+        raise ValueError(f"tree of {T} nodes does not fit {words} mask words")
+    out = np.zeros((T, words), dtype=np.uint64)
+    for i in range(T):
+        for j in range(T):
+            if vis[i, j]:
+                out[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return out
+
+
+def build_masks_words(inp, words: int) -> np.ndarray:
+    """Multi-word masks of every sequence packed like the tree rows: uint64 [N, words]."""
+    out = np.zeros((inp.total_tree_nodes, words), dtype=np.uint64)
+    for b in range(inp.batch):
+        lo, hi = int(inp.tree_offsets[b]), int(inp.tree_offsets[b + 1])
+        out[lo:hi] = ancestor_or_self_words(inp.parents[lo:hi], words)
+    return out
+
+
 def build_masks(inp) -> np.ndarray:
     """Masks of every sequence packed like the tree rows: uint64 [N]."""
     out = np.zeros(inp.total_tree_nodes, dtype=np.uint64)
@@ -164,7 +189,8 @@ def verify(inp) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     For every sequence b, tree node i and query head h: softmax attention of
     q[i, h] over the P_b prefix keys of KV head h // G followed by the tree keys
     of the nodes on i's root path.  Returns (o [N, Hq, D], lse [N, Hq], masks
-    [N] uint64), all computed in fp64 without splitting.
+    [N] uint64 -- [N, W] words when some tree has more than 64 nodes), all
+    computed in fp64 without splitting.
     [pith.science review, "What carries the argument"]
     """
     _check_shape(inp)
@@ -189,7 +215,10 @@ def verify(inp) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
             ob, lb = _attend(q, K, V, inp.softmax_scale, visible)
             o[lo + nodes, heads] = ob
             lse[lo + nodes, heads] = lb
-    return o, lse, build_masks(inp)
+    T_max = int(np.diff(inp.tree_offsets).max()) if inp.batch else 0
+    if T_max <= 64:
+        return o, lse, build_masks(inp)
+    return o, lse, build_masks_words(inp, -(-T_max // 64))
 
 
 def tree_rows_from_cache(inp) -> Tuple[np.ndarray, np.ndarray]:
