@@ -47,8 +47,10 @@
  *       tree_offsets      int32 [batch + 1]; tree of sequence b is rows
  *                         [tree_offsets[b], tree_offsets[b+1]); tree_offsets[0]
  *                         = 0 and tree_offsets[batch] = N
- *       mask              uint64 [N]; bit j of mask[tree_offsets[b] + i] set
- *                         iff local node j is i or an ancestor of i
+ *       mask              uint64 [N, W], W = ceil(max_tree_nodes / 64) words per
+ *                         node (W = 1 up to 64 nodes); bit j % 64 of word j / 64
+ *                         of row tree_offsets[b] + i is set iff local node j is
+ *                         i or an ancestor of i
  *   - Return codes report what the host can see: bad scalars, null or
  *     misaligned pointers, unsupported shapes, a workspace that is too small,
  *     launch failures.  Properties of device data (a bad parent array, a prefix
@@ -95,7 +97,9 @@ typedef struct {
   int32_t head_dim;           /* D in {64, 128} */
   int32_t block_size;         /* tokens per KV block; must be 64 */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
-  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size, 1..64 */
+  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size: 1..64 for the
+                                 fused verify, acceptance and commit; 1..256 for the split
+                                 path (build_mask, prefix, suffix, merge) */
   int32_t max_prefix_len;     /* upper bound on prefix_lens[b], 0..64*max_blocks_per_seq */
   int32_t total_tree_nodes;   /* N = tree_offsets[B] */
   int32_t num_blocks;         /* pool size: valid block ids are [0, num_blocks) */
@@ -118,7 +122,9 @@ size_t tree_attn_workspace_size(const ta_shape* shape);
 ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Build the ancestor-or-self mask words of every tree:
- * mask[i] = (parent[i] < 0 ? 0 : mask[parent[i]]) | (1 << i), per sequence.
+ * mask[i] = (parent[i] < 0 ? 0 : mask[parent[i]]) | (1 << i), per sequence,
+ * over W = ceil(max_tree_nodes / 64) words per node (trees of up to 256 nodes;
+ * one wave per tree up to 64 nodes, one 256-thread workgroup above).
  * Validates each parent (-1 or an earlier node of the same tree) and each tree
  * size (1..max_tree_nodes); a violation raises TA_ERR_BAD_TREE in the
  * workspace flag and that tree's words are zero.
@@ -140,8 +146,10 @@ ta_status tree_attn_prefix(const ta_shape* shape, const void* q, const void* k_c
                            hipStream_t stream);
 
 /* Suffix pass: attention of every tree query over the tree tokens whose bit is
- * set in its mask word (normally from tree_attn_build_mask).  Bits at or above
- * the tree size are ignored.  Writes o_suffix, lse_suffix (fp32).
+ * set in its mask words (normally from tree_attn_build_mask; W words per node
+ * as above).  Bits at or above the tree size are ignored.  Trees of more than
+ * 64 nodes are scored in segments of 64 keys folded by their log-sum-exps.
+ * Writes o_suffix, lse_suffix (fp32).
  * [pith.science review, "What carries the argument": draft-token piece] */
 ta_status tree_attn_suffix(const ta_shape* shape, const void* q, const void* k_tree,
                            const void* v_tree, const uint64_t* mask,
@@ -162,7 +170,9 @@ ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype,
                           hipStream_t stream);
 
 /* Fused verify: prefix pass + mask build + suffix pass + merge in one kernel
- * launch.  Writes out (shape->dtype) and lse_out (fp32, may be NULL).
+ * launch.  Writes out (shape->dtype) and lse_out (fp32, may be NULL).  Trees
+ * of up to 64 nodes (max_tree_nodes <= 64, else TA_ERR_UNSUPPORTED); larger
+ * trees take the split path.
  * [pith.science review, "What carries the argument"] */
 ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* block_table,

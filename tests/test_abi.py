@@ -52,7 +52,7 @@ def test_workspace_size_valid_and_monotone():
 
 
 @pytest.mark.parametrize("kw", [
-    dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(max_tree_nodes=65),
+    dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(max_tree_nodes=257),
     dict(batch=5000),
 ])
 def test_unsupported_shapes(kw):
@@ -119,3 +119,16 @@ def test_split_tokens_bounds():
         c = ta.split_tokens(s)
         assert c % 64 == 0 and 64 <= c <= 4096
         assert -(-s.max_prefix_len // c) <= 64    # at most 64 chunks per prefix
+
+
+@pytest.mark.parametrize("T", [65, 200, 256])
+def test_large_trees_split_path_only(T):
+    # trees of 65..256 nodes: the split path sizes a workspace; the fused verify,
+    # acceptance and commit refuse them before touching any pointer
+    s = shape(max_tree_nodes=T, total_tree_nodes=T)
+    assert ta.workspace_size(s) > 0
+    assert ta.split_tokens(s) > 0
+    lib = load()
+    assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None) == 2
+    assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), FAKE, 1 << 40, None) == 2
+    assert lib.tree_attn_accept_greedy(ctypes.byref(s), *([FAKE] * 7), FAKE, 1 << 40, None) == 2

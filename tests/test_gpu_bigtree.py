@@ -1,0 +1,89 @@
+"""GPU parity for trees of more than 64 nodes (up to 256) on the split path:
+multi-word masks bit for bit, and mask + prefix + suffix + merge against the
+fp64 oracle.  Also the draft-side shape: short prefixes under large trees
+(multi-round drafting attends with the same kernels)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, assert_close_lse, host, run_split, say, to_device, tolerances
+from helpers import random_tree
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _big(seed, trees, lens, *, dtype="bf16", Hq=8, Hkv=2, D=128):
+    rng = np.random.default_rng(seed)
+    return make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       prefix_lens=lens, trees=trees, rng=rng, spare_blocks=2)
+
+
+def _trees(seed):
+    rng = np.random.default_rng(seed)
+    return [random_tree(rng, 200), list(range(-1, 99)), [-1] + [0] * 64,
+            random_tree(rng, 256, forest_p=0.05), random_tree(rng, 70)]
+
+
+def test_multiword_masks_bit_exact():
+    import tree_attention_verify_attn_amd as ta
+    trees = _trees(1)
+    inp = _big(91, trees, [1] * len(trees))
+    d = to_device(inp, max_tree_nodes=256)
+    say("multi-word masks: trees of 200, 99, 65, 256, 70 nodes")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    got = mask.cpu().numpy().view(np.uint64)
+    want = oracle.build_masks_words(inp, 4)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_split_path_large_trees_matches_oracle(dtype, D):
+    import tree_attention_verify_attn_amd as ta
+    trees = _trees(2)
+    inp = _big(92, trees, [300, 0, 1000, 65, 7], dtype=dtype, D=D)
+    d = to_device(inp, max_tree_nodes=256)
+    say(f"split path, trees up to 256 nodes, {dtype} D={D}")
+    out, lse, _ = run_split(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(out), o_want, tol_o, "big-tree o")
+    assert_close_lse(host(lse), l_want, tol_l, "big-tree lse")
+
+
+def test_draft_side_short_prefixes_under_large_trees():
+    # multi-round drafting: the draft model's queries see a short context and a
+    # large tree; 8 sequences, prefixes 16..100, 128-node trees, GQA 32/8
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(93)
+    trees = [random_tree(rng, 128) for _ in range(8)]
+    lens = [int(x) for x in rng.integers(16, 101, size=8)]
+    inp = make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      prefix_lens=lens, trees=trees, rng=rng)
+    d = to_device(inp, max_tree_nodes=128)
+    say("draft-side shape: 8 x 128-node trees over 16..100-token prefixes")
+    out, lse, _ = run_split(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    assert_close(host(out), o_want, 2e-2, "draft-side o")
+    assert_close_lse(host(lse), l_want, 1e-3, "draft-side lse")
+
+
+def test_large_tree_bad_parent_flagged():
+    import tree_attention_verify_attn_amd as ta
+    trees = _trees(3)
+    inp = _big(94, trees, [10] * len(trees))
+    d = to_device(inp, max_tree_nodes=256)
+    d.parents[150] = 170       # a later node of the 200-node tree
+    say("multi-word mask: bad parent flagged")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 3
+    got = mask.cpu().numpy().view(np.uint64)
+    assert not got[:200].any()          # the bad tree's words are zero
+    want = oracle.build_masks_words(inp, 4)
+    np.testing.assert_array_equal(got[200:], want[200:])   # the others are intact

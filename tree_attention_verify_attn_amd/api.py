@@ -98,15 +98,22 @@ def _elem(shape: Shape) -> torch.dtype:
     return _TORCH_DTYPE[int(shape.dtype)]
 
 
+def _mask_shape(shape: Shape):
+    """[N] with one 64-bit word per node up to 64-node trees, else [N, W]."""
+    W = (int(shape.max_tree_nodes) + 63) // 64
+    return (shape.total_tree_nodes,) if W == 1 else (shape.total_tree_nodes, W)
+
+
 def build_mask(shape: Shape, parents: torch.Tensor, tree_offsets: torch.Tensor,
                workspace: torch.Tensor, mask: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     N = shape.total_tree_nodes
     _want(parents, "parents", torch.int32, (N,))
     _want(tree_offsets, "tree_offsets", torch.int32, (shape.batch + 1,))
+    mshape = _mask_shape(shape)
     if mask is None:
-        mask = torch.empty(N, dtype=torch.int64, device=parents.device)
-    _want(mask, "mask", torch.int64, (N,))
+        mask = torch.empty(mshape, dtype=torch.int64, device=parents.device)
+    _want(mask, "mask", torch.int64, mshape)
     _check(load().tree_attn_build_mask(ctypes.byref(shape), _ptr(parents), _ptr(tree_offsets),
                                        _ptr(mask), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "tree_attn_build_mask")
@@ -152,7 +159,7 @@ def suffix(shape: Shape, q, k_tree, v_tree, mask, tree_offsets,
     _want(q, "q", el, (N, Hq, D))
     _want(k_tree, "k_tree", el, (N, Hkv, D))
     _want(v_tree, "v_tree", el, (N, Hkv, D))
-    _want(mask, "mask", torch.int64, (N,))
+    _want(mask, "mask", torch.int64, _mask_shape(shape))
     _want(tree_offsets, "tree_offsets", torch.int32, (shape.batch + 1,))
     if o is None:
         o = torch.empty(N, Hq, D, dtype=torch.float32, device=q.device)

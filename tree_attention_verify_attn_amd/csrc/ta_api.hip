@@ -65,7 +65,7 @@ int check_shape(const ta_shape* s) {
   if (s->block_size != kBlock) return kErrUnsupported;
   if (s->max_blocks_per_seq < 1) return kErrInvalidArg;
   if (s->max_tree_nodes < 1) return kErrInvalidArg;
-  if (s->max_tree_nodes > kMaxTree) return kErrUnsupported;
+  if (s->max_tree_nodes > kMaxTreeSplit) return kErrUnsupported;
   if (s->max_prefix_len < 0) return kErrInvalidArg;
   if (static_cast<long long>(s->max_prefix_len) > static_cast<long long>(kBlock) * s->max_blocks_per_seq)
     return kErrInvalidArg;
@@ -203,6 +203,7 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.head_dim = s->head_dim;
   p.max_blocks = s->max_blocks_per_seq;
   p.max_tree = s->max_tree_nodes;
+  p.mask_words = cdiv(s->max_tree_nodes, 64);
   p.max_prefix = s->max_prefix_len;
   p.total_nodes = s->total_tree_nodes;
   p.num_blocks = s->num_blocks;
@@ -295,14 +296,17 @@ extern "C" {
 
 size_t tree_attn_workspace_size(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
-  const size_t a = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true)).total;
+  // the fused kernel serves trees of up to 64 nodes only
+  const size_t a = shape->max_tree_nodes <= kMaxTree
+                       ? layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true)).total
+                       : 0;
   const size_t b = layout_for(shape, choose_chunk(shape, false), auto_cap(shape, false)).total;
   return a > b ? a : b;
 }
 
 int32_t tree_attn_split_tokens(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
-  return choose_chunk(shape, true);
+  return choose_chunk(shape, shape->max_tree_nodes <= kMaxTree);
 }
 
 ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -330,7 +334,11 @@ ta_status tree_attn_build_mask(const ta_shape* shape, const int32_t* parents,
   Params p = base_params(shape, L, ws);
   p.parents = parents;
   p.tree_offsets = tree_offsets;
-  hipLaunchKernelGGL(mask_kernel, dim3(unsigned(shape->batch)), dim3(64), 0, stream, p, mask_out);
+  if (p.mask_words == 1)
+    hipLaunchKernelGGL(mask_kernel, dim3(unsigned(shape->batch)), dim3(64), 0, stream, p, mask_out);
+  else
+    hipLaunchKernelGGL(mask_words_kernel, dim3(unsigned(shape->batch)), dim3(kMaxTreeSplit), 0,
+                       stream, p, mask_out);
   return static_cast<ta_status>(launch_status());
 }
 
@@ -427,6 +435,7 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
                            float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!prefix_lens || !tree_offsets || !block_table) return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !parents || !out))
     return TA_ERR_INVALID_ARG;
@@ -460,6 +469,7 @@ ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const v
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!prefix_lens || !tree_offsets || !block_table || !k_cache || !v_cache)
     return TA_ERR_INVALID_ARG;
   if (shape->num_blocks < 1) return TA_ERR_INVALID_ARG;
@@ -493,6 +503,7 @@ ta_status tree_attn_commit_incache(const ta_shape* shape, const int32_t* parents
                                    size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens ||
       !k_cache || !v_cache)
     return TA_ERR_INVALID_ARG;
@@ -528,6 +539,7 @@ ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
                                   size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !bonus_token) return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!parents || !draft_tokens || !target_argmax))
     return TA_ERR_INVALID_ARG;
@@ -558,6 +570,7 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
                            hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
+  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens)
     return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!parents || !k_tree || !v_tree)) return TA_ERR_INVALID_ARG;

@@ -12,7 +12,8 @@ constexpr int kBlock = 64;        // tokens per KV-cache block
 constexpr int kThreads = 256;     // threads per workgroup of the small kernels (4 wave64)
 constexpr int kAttnThreads = 512; // threads per workgroup of the attention kernel (8 wave64)
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kMaxTree = 64;      // one 64-bit mask word per tree node
+constexpr int kMaxTree = 64;      // fused kernel and commit: one 64-bit mask word per tree node
+constexpr int kMaxTreeSplit = 256; // split path: up to four mask words per tree node
 constexpr int kMaxBatch = 2048;   // per-workgroup item table lives in LDS
 constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
@@ -76,6 +77,7 @@ struct Params {
   float* partials;           // [item slots][slot_floats]
   int batch, hq, hkv, group, head_dim;
   int max_blocks, max_tree, max_prefix, total_nodes, num_blocks;
+  int mask_words;            // 64-bit mask words per tree node: cdiv(max_tree, 64)
   int chunk;                 // prefix tokens per work item (multiple of 64)
   int rp_max;                // row passes per (sequence, head)
   int rows_slot;             // rows reserved per partial slot

@@ -101,7 +101,7 @@ __device__ __forceinline__ SeqInfo seq_info(const Params& p, int b, bool flag) {
 // tree offset | tree size << 24, pl[k] = prefix length, all validated (the
 // first workgroup flags bad data).  With it an item's facts need no global
 // read.  Returns the item count.
-constexpr int kTreeSizeShift = 24;  // tree offsets < 2^24 (<= 2048 trees of <= 64 nodes)
+constexpr int kTreeSizeShift = 23;  // tree offsets < 2^23 (<= 2048 trees of <= 256 nodes)
 constexpr int kSeqBits = 11;        // sequence index bits in a sort key (batch <= 2048)
 // Exclusive prefix sum of v over the workgroup's threads (in thread order) and
 // the total: a scan inside each wave, then the wave totals through LDS (one
@@ -1406,6 +1406,57 @@ __global__ void __launch_bounds__(64) mask_kernel(Params p, uint64_t* mask_out) 
   if (lane < T) mask_out[o0 + lane] = bad ? 0 : word;
 }
 
+// One workgroup of 256 threads per sequence for trees of up to 256 nodes:
+// thread i keeps node i's ancestor-or-self set in W <= 4 words and a link
+// to an ancestor; each of eight rounds ORs in the set of the linked node and
+// follows its link (through LDS), doubling the distance covered.  Output
+// mask_out[(off + i) * W + w], bit j % 64 of word j / 64.
+__global__ void __launch_bounds__(kMaxTreeSplit) mask_words_kernel(Params p, uint64_t* mask_out) {
+  __shared__ uint64_t anc_sh[kMaxTreeSplit * 4];
+  __shared__ int up_sh[kMaxTreeSplit];
+  __shared__ int bad_sh;
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int W = p.mask_words;
+  const int o0 = p.tree_offsets[b];
+  const int o1 = p.tree_offsets[b + 1];
+  const int T = o1 - o0;
+  const bool ok = o0 >= 0 && o1 >= o0 && o1 <= p.total_nodes && T <= p.max_tree;
+  if (!ok) {
+    if (i == 0) set_error(p.hdr, kErrBadTree);
+    return;
+  }
+  if (b == 0 && i == 0 && (p.tree_offsets[0] != 0 || p.tree_offsets[p.batch] != p.total_nodes))
+    set_error(p.hdr, kErrBadTree);
+  if (i == 0) bad_sh = 0;
+  __syncthreads();
+  int up = -1;
+  uint64_t anc[4] = {0, 0, 0, 0};
+  if (i < T) {
+    const int pr = p.parents[o0 + i];
+    const bool bad = !(pr == -1 || (pr >= 0 && pr < i));
+    if (bad) bad_sh = 1;
+    up = bad ? -1 : pr;
+    anc[i / 64] = uint64_t(1) << (i % 64);
+  }
+  for (int round = 0; round < 8; ++round) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) anc_sh[i * 4 + w] = anc[w];
+    up_sh[i] = up;
+    __syncthreads();
+    if (up >= 0) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) anc[w] |= anc_sh[up * 4 + w];
+      up = up_sh[up];
+    }
+    __syncthreads();
+  }
+  const bool bad = bad_sh != 0;
+  if (bad && i == 0) set_error(p.hdr, kErrBadTree);
+  if (i < T)
+    for (int w = 0; w < W; ++w) mask_out[size_t(o0 + i) * W + w] = bad ? 0 : anc[w];
+}
+
 // ========================================================== suffix kernel
 // One workgroup per (sequence, KV head, row pass); D/4 lanes per row, reading
 // q and the tree rows from global memory.  Writes normalised o and natural-log
@@ -1434,14 +1485,30 @@ __global__ void __launch_bounds__(kThreads) suffix_kernel(Params p) {
     const int r = r0 + rs;
     if (r >= rcount) break;
     const int rr = rlo + r;
-    const uint64_t word = p.mask_in[o0 + rr / G];
     const size_t orow = size_t(o0 + rr / G) * p.hq + g * G + rr % G;
     const T* kt = static_cast<const T*>(p.k_tree) + (size_t(o0) * p.hkv + g) * D;
     const T* vt = static_cast<const T*>(p.v_tree) + (size_t(o0) * p.hkv + g) * D;
-    TreeSrc<T, D> src{static_cast<const T*>(p.q) + orow * D, kt, vt, p.hkv * D, p.hkv * D, false};
-    float m, l;
-    float4 o;
-    tree_row<T, D>(src, Tn, d4, word, p.scale_log2, m, l, o);
+    // the tree in segments of 64 keys, one mask word each, folded by their
+    // log-sum-exps (base 2)
+    float m = -INFINITY, l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int seg = 0; seg * 64 < Tn; ++seg) {
+      const uint64_t word = p.mask_in[size_t(o0 + rr / G) * p.mask_words + seg];
+      const size_t koff = size_t(seg) * 64 * p.hkv * D;
+      TreeSrc<T, D> src{static_cast<const T*>(p.q) + orow * D, kt + koff, vt + koff, p.hkv * D,
+                        p.hkv * D, false};
+      float ms, ls;
+      float4 os;
+      tree_row<T, D>(src, min(64, Tn - seg * 64), d4, word, p.scale_log2, ms, ls, os);
+      if (ms == -INFINITY) continue;
+      const float mn = fmaxf(m, ms);
+      const float a = m == -INFINITY ? 0.f : exp2_fast(m - mn);
+      const float c = exp2_fast(ms - mn);
+      l = l * a + ls * c;
+      o = make_float4(o.x * a + os.x * c, o.y * a + os.y * c, o.z * a + os.z * c,
+                      o.w * a + os.w * c);
+      m = mn;
+    }
     const bool empty = m == -INFINITY;
     const float inv = empty ? 0.f : 1.f / l;
     *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * D + 4 * d4) =
