@@ -279,7 +279,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..5 (default 2); 6, 7: trees of more than 64 nodes")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--entry", choices=("verify", "split", "incache"), default="verify",
                     help="fused single launch (default), the four-call split path, or the fused "
@@ -326,6 +327,9 @@ def main() -> int:
 
     log(f"building workload cfg{args.config}")
     inp = make_config(args.config)
+    if inp.max_tree_nodes > 64 and args.entry != "split":
+        log("trees of more than 64 nodes run on the split path")
+        args.entry = "split"
     if args.entry == "incache":
         inp = incache_layout(inp)
     nbytes = algorithmic_bytes(inp)

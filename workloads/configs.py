@@ -44,6 +44,10 @@ CONFIG_NAMES = {
     4: "maverick-head-share: bf16 B=1 Hq=5 Hkv=1 D=128 prefix=8192 paged, 12-node tree, keys x2",
     5: "ragged-b256: bf16 B=256 Hq=32 Hkv=8 D=128 prefix lognormal(med 2048, sigma 1) "
        "clip[16,32768], trees {1,chain-4,12} p=.2/.5/.3",
+    # beyond the five verify workloads: trees of more than 64 nodes (split path)
+    6: "llama3.1-8b-verify-256-node-tree: bf16 B=1 Hq=32 Hkv=8 D=128 prefix=8192 paged, "
+       "random 256-node tree",
+    7: "draft-side-multi-round: bf16 B=8 Hq=32 Hkv=8 D=128 prefix U{16..100}, random 128-node trees",
 }
 
 
@@ -222,7 +226,8 @@ def make_inputs(
 
 def make_config(index: int, seed: Optional[int] = None, keep_logical: bool = False,
                 batch_override: Optional[int] = None) -> TreeVerifyInputs:
-    """Build config ``index`` (1..5).  ``batch_override`` shrinks configs 3 and 5 for tests
+    """Build config ``index`` (1..5: the verify workloads; 6, 7: trees of more
+    than 64 nodes).  ``batch_override`` shrinks configs 3, 5 and 7 for tests
     (same recipe, first draws only)."""
     if seed is None:
         seed = 1000 + index
@@ -257,4 +262,22 @@ def make_config(index: int, seed: Optional[int] = None, keep_logical: bool = Fal
         return make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
                            prefix_lens=lens, trees=trees, rng=rng, seed=seed,
                            name=name, keep_logical=keep_logical)
-    raise ValueError(f"config index must be 1..5, got {index}")
+    if index == 6:
+        tree = _random_tree(rng, 256)
+        return make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           prefix_lens=[8192], trees=[tree], rng=rng, seed=seed,
+                           name=name, keep_logical=keep_logical)
+    if index == 7:
+        B = 8 if batch_override is None else int(batch_override)
+        lens = rng.integers(16, 100 + 1, size=B)
+        trees = [_random_tree(rng, 128) for _ in range(B)]
+        return make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           prefix_lens=lens, trees=trees, rng=rng, seed=seed,
+                           name=name, keep_logical=keep_logical)
+    raise ValueError(f"config index must be 1..7, got {index}")
+
+
+def _random_tree(rng: np.random.Generator, T: int) -> List[int]:
+    """Seeded random topologically ordered parent array: node i's parent is
+    uniform over the earlier nodes."""
+    return [-1] + [int(rng.integers(0, i)) for i in range(1, T)]
