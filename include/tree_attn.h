@@ -91,7 +91,8 @@ typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
 /* Host-side description of one call.  Everything here is a host value; the
  * per-sequence data (prefix lengths, trees) stays on the device. */
 typedef struct {
-  int32_t batch;              /* B >= 1 (B <= 2048) */
+  int32_t batch;              /* B >= 1 (B <= 2048; and at most 2^18 groups:
+                                 B * Hkv * ceil(max_tree_nodes * Hq / Hkv / 64)) */
   int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* D in {64, 128} */
@@ -114,8 +115,9 @@ typedef struct {
  * A workspace must be zero-filled before its first use (tree_attn_workspace_init
  * does that).  A call that completes without a device-detected error leaves
  * the workspace's counters ready for the next call, so one workspace serves
- * call after call on one stream; after TA_ERR_TIMEOUT it must be zero-filled
- * again. */
+ * call after call on one stream, whatever each call's shape (as long as the
+ * workspace is large enough for it); after TA_ERR_TIMEOUT it must be
+ * zero-filled again. */
 size_t tree_attn_workspace_size(const ta_shape* shape);
 
 /* Zero-fill a workspace with a kernel (no hipMemset, so graph capture is safe). */

@@ -54,6 +54,8 @@ def test_workspace_size_valid_and_monotone():
 @pytest.mark.parametrize("kw", [
     dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(max_tree_nodes=257),
     dict(batch=5000),
+    # more than 2^18 groups (sequence, KV head, 64-row pass)
+    dict(batch=2048, num_q_heads=64, num_kv_heads=64, max_tree_nodes=256, total_tree_nodes=256),
 ])
 def test_unsupported_shapes(kw):
     s = shape(**kw)

@@ -215,6 +215,48 @@ def test_verify_workspace_reuse_and_determinism():
     _check_verify(inp, out3, lse3, "cfg2 third call")
 
 
+def test_verify_shared_workspace_changing_inputs():
+    """One workspace across calls whose data, batch, chunk counts and dtype
+    change from call to call (and with a device error in between): every call
+    combines its own chunk partials, never those a previous call left."""
+    import tree_attention_verify_attn_amd as ta
+    specs = [
+        ("two-long", dict(B=2, prefix_lens=(3000, 1500))),
+        ("two-long-new-data", dict(B=2, prefix_lens=(3000, 1500))),
+        ("three-mixed", dict(B=3, prefix_lens=(4000, 200, 2500))),
+        ("one-seq", dict(B=1, prefix_lens=(6000,))),
+        ("f32", dict(B=2, prefix_lens=(2000, 900), dtype="f32")),
+        ("two-long-again", dict(B=2, prefix_lens=(3000, 1500))),
+        ("one-seq-new-data", dict(B=1, prefix_lens=(6000,))),
+        # more groups than workgroups: items handed out by ticket
+        ("tickets", dict(B=160, prefix_lens=tuple(100 + (37 * i) % 1400 for i in range(160)))),
+        ("two-long-after-tickets", dict(B=2, prefix_lens=(3000, 1500))),
+    ]
+    cases = []
+    for k, (name, kw) in enumerate(specs):
+        kw = dict(kw)
+        dtype = kw.pop("dtype", "bf16")
+        inp = small_inputs(300 + k, dtype=dtype, Hq=8, Hkv=2, D=128,
+                           trees=[TREE_12] * kw["B"], **kw)
+        cases.append((name, inp, to_device(inp)))
+    ws = max((c[2].workspace for c in cases), key=lambda t: t.numel())
+    for name, inp, d in cases:
+        d.workspace = ws
+    for rep in range(2):
+        for name, inp, d in cases:
+            say(f"shared workspace: {name} pass {rep}")
+            out, lse = run_verify(d)
+            assert ta.get_error(ws) == 0, name
+            _check_verify(inp, out, lse, f"shared workspace {name}")
+        # a call that flags a bad prefix length, then clean calls again
+        name, inp, d = cases[2]
+        d.prefix_lens[1] = inp.max_prefix_len + 1
+        say("shared workspace: bad prefix length")
+        run_verify(d)
+        assert ta.get_error(ws) == 6
+        d.prefix_lens[1] = int(inp.prefix_lens[1])
+
+
 def test_verify_block_permutation_bit_identical():
     inp = make_config(3, batch_override=8)
     d = to_device(inp)

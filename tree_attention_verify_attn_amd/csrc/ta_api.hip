@@ -73,6 +73,9 @@ int check_shape(const ta_shape* s) {
   if (s->num_blocks < 0 || (s->max_prefix_len > 0 && s->num_blocks < 1)) return kErrInvalidArg;
   if (s->split_tokens < 0 || s->split_tokens % kBlock != 0) return kErrInvalidArg;
   if (s->split_tokens > 4096) return kErrUnsupported;
+  const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
+                           cdiv(s->max_tree_nodes * (s->num_q_heads / s->num_kv_heads), kRowsPerPass);
+  if (groups > kMaxGroups) return kErrUnsupported;
   if (!(s->softmax_scale <= 0.f || isfinite(s->softmax_scale))) return kErrInvalidArg;
   return kOk;
 }
@@ -129,7 +132,8 @@ int grid_capacity(const ta_shape* s, bool fused) {
   int cus = device_info().cus;
   if (cus <= 0) cus = 256;  // no device: size for a full MI355X, one workgroup per CU
   const int occ = occupancy(attn_kernel_ptr(s, fused), attn_dyn_lds(s, fused));
-  return cus * (occ > 0 ? occ : 1);
+  const int cap = cus * (occ > 0 ? occ : 1);
+  return cap < kBarrierSlots ? cap : kBarrierSlots;
 }
 
 // Prefix tokens per work item.  Every XCD gets the groups (sequence, KV head,
@@ -181,14 +185,17 @@ WsLayout layout_for(const ta_shape* s, int chunk, int min_item_slots = 0) {
   int rows = s->max_tree_nodes * G;
   if (rows > kRowsPerPass) rows = kRowsPerPass;
   L.rows_slot = 16 * cdiv(rows, 16);
-  L.slot_floats = L.rows_slot * (D + 2);
+  L.slot_floats = L.rows_slot * (D + 2);  // fp32 o rows, then m and l per row
   L.num_groups = s->batch * s->num_kv_heads * L.rp_max;
   L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
   // large batches: dense per-XCD numbering from a prefix table; small: static
   L.item_slots = L.num_groups * L.s_max;
   if (L.item_slots < min_item_slots) L.item_slots = min_item_slots;
   L.arrive_off = sizeof(WsHeader);
-  L.partial_off = align256(L.arrive_off + sizeof(unsigned) * kCounterStride * size_t(L.num_groups));
+  // barrier pairs, then ticket counters (the kernel addresses both from the
+  // region's start); neither depends on the shape
+  L.partial_off = L.arrive_off + sizeof(unsigned) * (size_t(kCounterStride) * kBarrierSlots + kMaxGroups);
+  static_assert(sizeof(WsHeader) % 256 == 0, "barrier region and partials stay 256-byte aligned");
   L.total = L.partial_off +
             size_t(L.item_slots) * L.slot_floats * sizeof(float);
   return L;
@@ -263,6 +270,7 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
   if (occ < 1) return kErrUnsupported;  // tree rows + item table exceed the LDS
   const int cap = cus * occ;
   int first = L.item_slots < cap ? L.item_slots : cap;
+  if (first > kBarrierSlots) first = kBarrierSlots;  // one barrier pair per item of the first round
   if (first < 1) first = 1;
   p.first_round = first;
   hipLaunchKernelGGL((attn_kernel<T, D, FUSED>), dim3(unsigned(first)), dim3(kAttnThreads),

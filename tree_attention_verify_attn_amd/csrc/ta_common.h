@@ -36,6 +36,8 @@ enum : int {
 };
 
 constexpr int kCounterStride = 64;  // unsigned words between two counters: one 256-byte line each
+constexpr int kBarrierSlots = 1024; // group barriers in the workspace's fixed region (grid size bound)
+constexpr int kMaxGroups = 1 << 18; // ticket arrival counters: batch * kv heads * row passes, at most
 
 // First 768 bytes of every workspace: each field on a cache line of its own,
 // so that the device-scope atomics on one do not queue behind those on another.
@@ -73,7 +75,8 @@ struct Params {
   void* out;                 // fused: shape dtype;  prefix/suffix: fp32
   float* lse_out;            // may be null in fused mode
   WsHeader* hdr;
-  unsigned* arrive;          // per group arrival counters, kCounterStride apart
+  unsigned* arrive;          // [kBarrierSlots] (arrival counter, sense) pairs, kCounterStride
+                             // apart, then [kMaxGroups] ticket arrival counters
   float* partials;           // [item slots][slot_floats]
   int batch, hq, hkv, group, head_dim;
   int max_blocks, max_tree, max_prefix, total_nodes, num_blocks;

@@ -695,8 +695,18 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // row), the tree's parent array and, last, the chunk's block ids (lane j:
   // block j).  All of it is complete before the first LDS transfer is issued,
   // so no later wait for these values can hold up the transfers.
-  unsigned* const counter = p.arrive + size_t(it.grp) * kCounterStride;
-  unsigned* const sense = counter + kCounterStride / 2;
+  // The group's meeting words, at places that do not depend on the call's
+  // shape, so that calls of any shape can share a workspace.  Without tickets
+  // every item number is below the grid size: the pair (arrival counter,
+  // sense) of the group's first item number in the barrier region.  With
+  // tickets: the group's arrival counter in the ticket-counter region, which
+  // follows the barrier region (the sense word read below is then that of a
+  // clamped index and goes unused).
+  const int first_item = slot_index - it.s;
+  unsigned* const bar = p.arrive + size_t(min(first_item, kBarrierSlots - 1)) * kCounterStride;
+  unsigned* const sense = bar + kCounterStride / 2;
+  unsigned* const counter =
+      solo_combine ? p.arrive + size_t(kBarrierSlots) * kCounterStride + size_t(it.grp) : bar;
   // nothing of the previous item is still in flight (free for the first item):
   // a wait the compiler would otherwise place before reusing registers of the
   // previous item lands here, not between the loads of this trip
@@ -1158,21 +1168,36 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     return;
   }
 
-  // ---- chunk partial -> workspace (device-coherent stores)
+  // ---- chunk partial -> workspace (device-coherent stores): the fp32 o rows
+  // (D floats each), then the running max m and sum l of every row.  The o
+  // rows are first gathered in LDS (16-byte pieces XOR-swizzled by row
+  // against bank conflicts), so that the stores to the workspace cover whole
+  // cache lines: lane i stores bytes [16 i, 16 i + 16) of the slot's o rows.
   {
+    constexpr int PER_ROW = D / 4;  // 16-byte pieces per o row
+    static_assert(kRowsPerPass * D * 4 <= Gm::SLOTB, "staged o rows fit one ring slot");
+    unsigned char* stage = ring;    // free once the key parts are merged
     float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
     const uint32_t sbytes = uint32_t(p.slot_floats) * 4u;
+    __syncthreads();
     if (kp == 0 && active) {
       const int r = 16 * rt + lr;
       if (r < rcount) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          coherent_store16(slotp, sbytes, uint32_t(r * D + 16 * dt + 4 * kq) * 4u, oacc[dt]);
+          *reinterpret_cast<floatx4*>(stage + (r * PER_ROW + ((4 * dt + kq) ^ (r & 15))) * 16) = oacc[dt];
         if (kq == 0) {
           coherent_store4(slotp, sbytes, uint32_t(p.rows_slot * D + r) * 4u, m_run);
           coherent_store4(slotp, sbytes, uint32_t(p.rows_slot * D + p.rows_slot + r) * 4u, l_run);
         }
       }
+    }
+    __syncthreads();
+    for (int i = tid; i < rcount * PER_ROW; i += kAttnThreads) {
+      const int r = i / PER_ROW;
+      const int c = i % PER_ROW;
+      coherent_store16(slotp, sbytes, uint32_t(i) * 16u,
+                       *reinterpret_cast<const floatx4*>(stage + (r * PER_ROW + (c ^ (r & 15))) * 16));
     }
   }
 
