@@ -1260,6 +1260,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     constexpr int L4 = D / 4;
     constexpr int NSLOT = kAttnThreads / L4;
     constexpr int QMAX = kMaxSplits / NSLOT;
+    static_assert((NSLOT & (NSLOT - 1)) == 0, "row slots are a power of two");
     // QG row slots per row: enough that QMAX loads per lane cover the S
     // partials, and no more than lets all of this workgroup's rows go in one
     // pass
@@ -1304,8 +1305,17 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       for (int j = 0; j < QMAX; ++j) mloc = fmaxf(mloc, mq[j]);
       if (d4 == 0) red_m[rs] = mloc;
       __syncthreads();
+      // LDS reads in groups of four, each group issued before any of it is
+      // used (index clamped into the row slots, result masked): QG / 4
+      // round trips rather than QG
       float M = -INFINITY;
-      for (int x = 0; x < QG; ++x) M = fmaxf(M, red_m[rb * QG + x]);
+      for (int x0 = 0; x0 < QG; x0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = red_m[(rb * QG + x0 + u) & (NSLOT - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) M = x0 + u < QG ? fmaxf(M, v[u]) : M;
+      }
       float L = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       if (M != -INFINITY) {
@@ -1325,11 +1335,21 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       if (qg == 0 && valid) {
         float Lt = 0.f;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int x = 0; x < QG; ++x) {
-          const int sx = rb * QG + x;
-          Lt += red_l[sx];
-          const float4 ox = *reinterpret_cast<const float4*>(red_o + sx * D + 4 * d4);
-          o.x += ox.x; o.y += ox.y; o.z += ox.z; o.w += ox.w;
+        for (int x0 = 0; x0 < QG; x0 += 4) {
+          float lx[4];
+          float4 ox[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int sx = (rb * QG + x0 + u) & (NSLOT - 1);
+            lx[u] = red_l[sx];
+            ox[u] = *reinterpret_cast<const float4*>(red_o + sx * D + 4 * d4);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (x0 + u < QG) {
+              Lt += lx[u];
+              o.x += ox[u].x; o.y += ox[u].y; o.z += ox[u].z; o.w += ox[u].w;
+            }
         }
         float lse = -INFINITY;
         if (M != -INFINITY) {
