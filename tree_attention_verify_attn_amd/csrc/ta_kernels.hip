@@ -162,8 +162,56 @@ __device__ __forceinline__ void block_sum2_max(int& a, int& b, int& c, int* scra
 // tokens with which every item fits in the first round (the sum of the
 // groups' chunk counts stays within the grid) and no group has more than
 // kMaxSplits chunks.  `chunk` returns the chunk in force.
+// Ascending bitonic sort of np keys (np a power of two, np <= kMaxBatch);
+// element i = q * kAttnThreads + thread lives in keys[q] of that thread.
+// Partners less than a wave apart meet by lane shuffles, partners in other
+// waves through two LDS buffers in turn (xbuf: 2 * kMaxBatch ints, one
+// barrier per such step), partners in another slot of the same thread in
+// registers.  Every thread must call it.
+constexpr int kSortSlots = kMaxBatch / kAttnThreads;
+__device__ void bitonic_sort(int (&keys)[kSortSlots], int np, int* xbuf) {
+  const int tid = threadIdx.x;
+  int b = 0;
+  for (int k = 2; k <= np; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= kAttnThreads) {
+        const int qd = jj / kAttnThreads;
+#pragma unroll
+        for (int q = 0; q < kSortSlots; ++q) {
+          const int qp = q ^ qd;
+          if (qp > q && qp < kSortSlots) {
+            const bool up = ((q * kAttnThreads + tid) & k) == 0;
+            const int lo = min(keys[q], keys[qp]), hi = max(keys[q], keys[qp]);
+            keys[q] = up ? lo : hi;
+            keys[qp] = up ? hi : lo;
+          }
+        }
+      } else {
+        int other[kSortSlots];
+        if (jj >= 64) {
+          int* xb = xbuf + b * kMaxBatch;
+#pragma unroll
+          for (int q = 0; q < kSortSlots; ++q) xb[q * kAttnThreads + tid] = keys[q];
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < kSortSlots; ++q) other[q] = xb[q * kAttnThreads + (tid ^ jj)];
+          b ^= 1;  // the next exchange writes the other buffer, so no second barrier
+        } else {
+#pragma unroll
+          for (int q = 0; q < kSortSlots; ++q) other[q] = __shfl_xor(keys[q], jj);
+        }
+#pragma unroll
+        for (int q = 0; q < kSortSlots; ++q) {
+          const int i = q * kAttnThreads + tid;
+          const bool keep_min = ((i & k) == 0) == ((i & jj) == 0);
+          keys[q] = keep_min ? min(keys[q], other[q]) : max(keys[q], other[q]);
+        }
+      }
+    }
+}
+
 __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* perm, int* scratch,
-                           int& chunk) {
+                           int* xbuf, int& chunk) {
   const int tid = threadIdx.x;
   const int n = p.batch;
   const int per = cdiv(n, kAttnThreads);
@@ -220,30 +268,25 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
   } else {
     // processing order: keys (length class, index) ascending = longest first
     const int np = [&] { int v = 1; while (v < n) v <<= 1; return v; }();
-    for (int i = tid; i < np; i += kAttnThreads) {
-      int key = 0x7fffffff;  // padding sorts last
+    __syncthreads();  // pl[] of every sequence is in LDS
+    int keys[kSortSlots];
+#pragma unroll
+    for (int q = 0; q < kSortSlots; ++q) {
+      const int i = q * kAttnThreads + tid;
+      keys[q] = 0x7fffffff;  // padding sorts last
       if (i < n) {
         const int P = pl[i];
         const int cls = 31 - __clz(P > 1 ? P : 1);  // 0..15
-        key = ((15 - cls) << kSeqBits) | i;
+        keys[q] = ((15 - cls) << kSeqBits) | i;
       }
-      perm[i] = key;
+    }
+    bitonic_sort(keys, np, xbuf);
+#pragma unroll
+    for (int q = 0; q < kSortSlots; ++q) {
+      const int i = q * kAttnThreads + tid;
+      if (i < np) perm[i] = keys[q];
     }
     __syncthreads();
-    for (int k = 2; k <= np; k <<= 1)
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < np; i += kAttnThreads) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const int a = perm[i], b = perm[ixj];
-            if ((a > b) == ((i & k) == 0)) {
-              perm[i] = b;
-              perm[ixj] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
     // facts and item prefix in processing order (gathered through registers,
     // written back in place after the scan's barrier)
     int g_ot[kPerMax], g_pl[kPerMax];
@@ -1398,7 +1441,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   if (p.single) {
     items = p.single_items;  // the tree offsets are checked by the launch's first item
   } else {
-    items = build_table(p, cum, ot, pl, perm, sm.scratch, chunk);
+    // the sort's exchange buffers use the ring, which holds no block yet
+    static_assert(2 * kMaxBatch * sizeof(int) <= size_t(Gm::SLOTB), "sort buffers fit one ring slot");
+    items = build_table(p, cum, ot, pl, perm, sm.scratch, reinterpret_cast<int*>(ring), chunk);
   }
 
   // items in increasing order: first blockIdx.x, then from the ticket counter.
