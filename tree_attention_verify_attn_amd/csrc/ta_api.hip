@@ -255,6 +255,25 @@ const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
   return fused ? attn_ptr<float, 64, true>() : attn_ptr<float, 64, false>();
 }
 
+// The split path's tree piece: one workgroup per (sequence, KV head, row
+// pass), its dynamic LDS a ring of as many 64-node segments as fit.
+template <typename T, int D>
+int launch_suffix(const ta_shape* s, Params p, unsigned grid, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&suffix_kernel<T, D>);
+  const size_t slot = ring_slot_bytes(s);
+  const size_t room = size_t(kLdsBytes) - sizeof(SmemMisc) - 256;
+  int ns = int(room / slot);
+  if (ns > kMaxRingSlots) ns = kMaxRingSlots;
+  if (ns < 1) return kErrUnsupported;
+  p.ns = ns;
+  p.tree_lds_half = 0;
+  const size_t dyn = size_t(ns) * slot;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn)) != hipSuccess)
+    return kErrHip;
+  hipLaunchKernelGGL((suffix_kernel<T, D>), dim3(grid), dim3(kAttnThreads), dyn, stream, p);
+  return launch_status();
+}
+
 template <typename T, int D, bool FUSED>
 int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
   const void* kern = attn_ptr<T, D, FUSED>();
@@ -400,18 +419,13 @@ ta_status tree_attn_suffix(const ta_shape* shape, const void* q, const void* k_t
   p.out = o_suffix;
   p.lse_out = lse_suffix;
   const unsigned grid = unsigned(L.num_groups);
-  if (shape->dtype == TA_DTYPE_BF16) {
-    if (shape->head_dim == 128)
-      hipLaunchKernelGGL((suffix_kernel<uint16_t, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((suffix_kernel<uint16_t, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
-  } else {
-    if (shape->head_dim == 128)
-      hipLaunchKernelGGL((suffix_kernel<float, 128>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((suffix_kernel<float, 64>), dim3(grid), dim3(kThreads), 0, stream, p);
-  }
-  return static_cast<ta_status>(launch_status());
+  if (shape->dtype == TA_DTYPE_BF16)
+    st = shape->head_dim == 128 ? launch_suffix<uint16_t, 128>(shape, p, grid, stream)
+                                : launch_suffix<uint16_t, 64>(shape, p, grid, stream);
+  else
+    st = shape->head_dim == 128 ? launch_suffix<float, 128>(shape, p, grid, stream)
+                                : launch_suffix<float, 64>(shape, p, grid, stream);
+  return static_cast<ta_status>(st);
 }
 
 ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype, const float* o_a,

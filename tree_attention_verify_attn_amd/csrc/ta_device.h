@@ -29,25 +29,6 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ float from_f(float f) { return f; }
 };
 
-// Dot product of 16 bytes of q with 16 bytes of k, accumulated in fp32.
-__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, uint16_t) {
-  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-  const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = fmaf(bf16_to_f32(static_cast<uint16_t>(av[i])), bf16_to_f32(static_cast<uint16_t>(bv[i])), acc);
-    acc = fmaf(bf16_to_f32(static_cast<uint16_t>(av[i] >> 16)), bf16_to_f32(static_cast<uint16_t>(bv[i] >> 16)), acc);
-  }
-  return acc;
-}
-__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, float) {
-  acc = fmaf(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, b.x), acc);
-  acc = fmaf(__builtin_bit_cast(float, a.y), __builtin_bit_cast(float, b.y), acc);
-  acc = fmaf(__builtin_bit_cast(float, a.z), __builtin_bit_cast(float, b.z), acc);
-  acc = fmaf(__builtin_bit_cast(float, a.w), __builtin_bit_cast(float, b.w), acc);
-  return acc;
-}
-
 // -------------------------------------------------------------- math
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
@@ -129,10 +110,6 @@ __device__ __forceinline__ uint64_t tree_mask_lanes(int p, int T, bool& bad) {
 __device__ __forceinline__ uint64_t tree_mask_wave(const int32_t* parents, int T, bool& bad) {
   const int lane = threadIdx.x & 63;
   return tree_mask_lanes(lane < T ? parents[lane] : -1, T, bad);
-}
-
-__device__ __forceinline__ uint64_t low_bits(int T) {
-  return T >= 64 ? ~uint64_t(0) : ((uint64_t(1) << T) - 1);
 }
 
 }  // namespace ta

@@ -13,7 +13,7 @@
 //   mask_kernel      ancestor-or-self mask words of every tree (one wave per tree)
 //   attn_kernel      prefix pass; with FUSED it also builds the tree mask, runs
 //                    the tree piece and merges (the fused verify)
-//   suffix_kernel    tree piece on its own (split path)
+//   suffix_kernel    tree piece on its own (split path), on the same MFMA path
 //   merge_kernel     merge of two (o, lse) results (split path)
 //
 // attn_kernel, one work item = sequence b, KV head g, row pass rp, prefix chunk s,
@@ -388,99 +388,6 @@ __device__ __forceinline__ Item decode_single(const Params& p, int li) {
   return it;
 }
 
-// ====================================================== suffix (tree) piece
-// D/4 consecutive lanes (one "row slot") compute the tree piece of one grouped
-// query row: the keys are the tree nodes whose bit is set in `word`.  Lane d4
-// of the slot scores keys d4, d4 + D/4, ... and owns output elements
-// [4*d4, 4*d4 + 4).  Returns the max m (log2 units: scores carry
-// softmax_scale*log2 e), l = sum of 2^(s - m) and the lane's four unnormalised
-// outputs.  No visible key gives m = -inf, l = 0, o = 0.
-// [draft-token piece that needs the tree mask: pith.science review,
-// "What carries the argument"]
-template <typename T, int D>
-struct TreeSrc {
-  const T* q;        // this row's query, D elements
-  const T* k;        // row j of tree K at k + j * k_stride (chunks XOR-swizzled if swz)
-  const T* v;        // row j of tree V at v + j * v_stride (swizzled like k)
-  int k_stride, v_stride;
-  bool swz;
-};
-
-template <typename T, int D>
-__device__ void tree_row(const TreeSrc<T, D>& src, int Tn, int d4, uint64_t word,
-                         float scale_log2, float& m_out, float& l_out, float4& o_out) {
-  constexpr int L4 = D / 4;
-  constexpr int KPL = kMaxTree / L4;  // keys scored per lane
-  constexpr int KCH = D * int(sizeof(T)) / 16;
-  constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;
-  word &= low_bits(Tn);
-  const uint4* q16 = reinterpret_cast<const uint4*>(src.q);
-  float s[KPL];
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) {
-    const int jj = d4 + L4 * k;
-    const bool vis = (word >> jj) & 1;
-    float dot = 0.f;
-    if (vis) {
-      const uint4* krow = reinterpret_cast<const uint4*>(src.k + size_t(jj) * src.k_stride);
-#pragma unroll 4
-      for (int c = 0; c < KCH; ++c) {
-        const int pc = src.swz ? (c ^ (jj & SWZ)) : c;
-        dot = dot16(q16[c], krow[pc], dot, T());
-      }
-    }
-    s[k] = vis ? dot * scale_log2 : -INFINITY;
-    m = fmaxf(m, s[k]);
-  }
-#pragma unroll
-  for (int x = 1; x < L4; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, L4));
-  o_out = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (m == -INFINITY) {
-    m_out = -INFINITY;
-    l_out = 0.f;
-    return;
-  }
-  float pk[KPL];
-  float l = 0.f;
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) {
-    pk[k] = s[k] == -INFINITY ? 0.f : exp2_fast(s[k] - m);
-    l += pk[k];
-  }
-#pragma unroll
-  for (int x = 1; x < L4; x <<= 1) l += __shfl_xor(l, x, L4);
-  uint64_t bits = word;
-  while (bits) {
-    const int jj = __builtin_ctzll(bits);
-    bits &= bits - 1;
-    float mine = pk[0];
-#pragma unroll
-    for (int k = 1; k < KPL; ++k) mine = (jj / L4 == k) ? pk[k] : mine;
-    const float pj = __shfl(mine, jj % L4, L4);
-    // element 4*d4 sits in 16-byte chunk (4*d4*sizeof(T))/16 of the row
-    constexpr int EPC = 16 / int(sizeof(T));  // elements per chunk
-    const int vc = (4 * d4) / EPC;
-    const int vcs = src.swz ? (vc ^ (jj & SWZ)) : vc;
-    const T* vrow = src.v + size_t(jj) * src.v_stride + vcs * EPC + (4 * d4) % EPC;
-    float v[4];
-    if constexpr (sizeof(T) == 2) {
-      const uint2 raw = *reinterpret_cast<const uint2*>(vrow);
-      v[0] = bf16_to_f32(uint16_t(raw.x)); v[1] = bf16_to_f32(uint16_t(raw.x >> 16));
-      v[2] = bf16_to_f32(uint16_t(raw.y)); v[3] = bf16_to_f32(uint16_t(raw.y >> 16));
-    } else {
-      const float4 raw = *reinterpret_cast<const float4*>(vrow);
-      v[0] = raw.x; v[1] = raw.y; v[2] = raw.z; v[3] = raw.w;
-    }
-    o_out.x = fmaf(pj, v[0], o_out.x);
-    o_out.y = fmaf(pj, v[1], o_out.y);
-    o_out.z = fmaf(pj, v[2], o_out.z);
-    o_out.w = fmaf(pj, v[3], o_out.w);
-  }
-  m_out = m;
-  l_out = l;
-}
-
 // =========================================================== prefix piece
 // LDS of one workgroup: a ring of NS KV slots (declared in attn_kernel), the
 // tree rows and the sequence table (dynamic), and SmemMisc.
@@ -698,7 +605,10 @@ constexpr float kRescaleSlack = 8.f;
 // One work item on the 8 waves of a workgroup.  Wave w takes row tile w % 4
 // and key half w / 4 of every 64-key block, with its own online-softmax state;
 // the two halves of a row tile are merged once, at the end of the item.
-template <typename T, int D, bool FUSED>
+// SUFFIX: the tree piece of the split path on its own -- no prefix, the tree
+// keys streamed through the ring in segments of 64 nodes, each under its
+// word of the precomputed ancestor-or-self mask (p.mask_in), fp32 outputs.
+template <typename T, int D, bool FUSED, bool SUFFIX = false>
 __device__ __forceinline__ void process_item(const Params& p, unsigned char* ring,
                                              unsigned char* tree_lds,
                                              SmemMisc& sm, const Item& it, int slot_index,
@@ -755,7 +665,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // previous item lands here, not between the loads of this trip
   wait_vm<0>();
   int sense_read = 0;  // hidden: a compiler wait for it would stall the loads below
-  if (tid == 0) sense_read = hidden_load<true>(reinterpret_cast<const int*>(sense));
+  if constexpr (!SUFFIX)
+    if (tid == 0) sense_read = hidden_load<true>(reinterpret_cast<const int*>(sense));
   uint4 qv[QCH];
   {
     const int r = 16 * rt + lr;
@@ -797,10 +708,22 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     if (first_of_launch && w == 0) toff = hidden_load(p.tree_offsets + (lane & 1));
   }
   int my_id = -1;
-  {
+  if constexpr (!SUFFIX) {
     const int lb = it.s * cpb + lane;
     if (lane < cpb + (extra_lanes ? 2 : 0) && lb < p.max_blocks)
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
+  }
+  // suffix: this lane's row's mask words, one per 64-node segment
+  constexpr int kSegMax = kMaxTreeSplit / 64;
+  uint64_t segw[kSegMax] = {};
+  if constexpr (SUFFIX) {
+    const int r = 16 * rt + lr;
+    if (active && r < rcount) {
+      const size_t node = size_t(si.off + (rlo + r) / G);
+#pragma unroll
+      for (int sg = 0; sg < kSegMax; ++sg)
+        if (sg < p.mask_words) segw[sg] = p.mask_in[node * p.mask_words + sg];
+    }
   }
   wait_vm<0>();
   const unsigned sense0 = unsigned(settle(sense_read));
@@ -828,7 +751,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // are finite.
   unsigned char* tk = tree_lds;
   unsigned char* tv = tree_lds + p.tree_lds_half;
-  const int tree_rows = p.tree_lds_half / ROWB;  // staged rows (>= tree size)
+  const int tree_rows = SUFFIX ? kBlock : p.tree_lds_half / ROWB;  // staged rows (>= tree size)
   if (with_tree) {
     const int Tn = si.T;
     const int ninstr = p.tree_lds_half / 1024;
@@ -943,7 +866,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // reads are clamped to the staging area).  Lane (row lr, group kq) ends up
   // holding scores of keys kp KS + 16 a + 4 kq + i (a < KS / 16, i < 4).
   auto compute = [&](auto tree_tag, auto ks_tag, auto mask_tag, const unsigned char* kb,
-                     const unsigned char* vb, int nvalid) {
+                     const unsigned char* vb, int nvalid, uint64_t tword) {
     constexpr bool kTree = decltype(tree_tag)::value;
     constexpr bool kMasked = kTree || decltype(mask_tag)::value;  // else every key is visible
     constexpr int KS = decltype(ks_tag)::value;  // 16 or 32 keys
@@ -953,7 +876,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     uint64_t word = 0;
     if constexpr (kTree) {
       const int r = 16 * rt + lr;
-      word = r < rcount ? sm.mask[(rlo + r) / G] : 0;
+      word = SUFFIX ? tword : (r < rcount ? sm.mask[(rlo + r) / G] : 0);
     }
     // every LDS read of the block is issued before the first MFMA
     uint4 kf[NA][QCH];
@@ -1118,7 +1041,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
         }
       }
       if constexpr (decltype(act_tag)::value)
-        compute(std::false_type{}, ks_tag, mask_tag, slot, slot + BLKB, nv);
+        compute(std::false_type{}, ks_tag, mask_tag, slot, slot + BLKB, nv, 0);
       raw_barrier();
       if (j + NS < nblk) issue(j + NS);
     }
@@ -1130,7 +1053,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     if (with_tree) {
       raw_barrier();  // staged rows of every wave and the mask words are in LDS
       if constexpr (decltype(act_tag)::value)
-        compute(std::true_type{}, ks_tag, std::true_type{}, tk, tv, 0);
+        compute(std::true_type{}, ks_tag, std::true_type{}, tk, tv, 0, 0);
     }
     if (bad != 0) {
       stream(ks_tag, std::true_type{}, act_tag, 0, nblk);
@@ -1140,7 +1063,48 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       stream(ks_tag, std::true_type{}, act_tag, nfull, nblk);
     }
   };
-  if (KP == 4) {
+  // suffix: the tree's 64-node segments go through the ring like KV blocks
+  // (the rows of the segment, clamped to the last node, gathered from the
+  // [node, KV head, D] tree tensors: KI transfers per wave and tensor)
+  const int nseg = SUFFIX ? cdiv(si.T, kBlock) : 0;
+  auto stage = [&](int sg) {
+    unsigned char* sk = ring + (sg % NS) * SLOTB;
+    for (int m = w; m < BLKB / 1024; m += kAttnWaves) {
+      const int u = m * 64 + lane;
+      const int t = min(kBlock * sg + u / KCH, si.T - 1);
+      const int pc = u % KCH;
+      const int c = pc ^ ((u / KCH) & SWZ);
+      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff) + c * 16,
+                sk + m * 1024);
+      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff) + c * 16,
+                sk + BLKB + m * 1024);
+    }
+  };
+  auto segments = [&](auto ks_tag, auto act_tag) {
+    // unrolled, so that segw is indexed by constants and stays in registers
+#pragma unroll
+    for (int sg = 0; sg < kSegMax; ++sg) {
+      if (sg >= nseg) break;
+      unsigned char* slot = ring + (sg % NS) * SLOTB;
+      wait_blocks<KI, NSMAX>(min(NS - 1, nseg - 1 - sg));
+      raw_barrier();
+      if constexpr (decltype(act_tag)::value)
+        compute(std::true_type{}, ks_tag, std::true_type{}, slot, slot + BLKB, 0, segw[sg]);
+      raw_barrier();
+      if (sg + NS < nseg) stage(sg + NS);
+    }
+  };
+  if constexpr (SUFFIX) {
+    for (int sg = 0; sg < NS && sg < nseg; ++sg) stage(sg);
+    if (KP == 4) {
+      if (active) segments(std::integral_constant<int, 16>{}, std::true_type{});
+      else segments(std::integral_constant<int, 16>{}, std::false_type{});
+    } else {
+      if (active) segments(std::integral_constant<int, 32>{}, std::true_type{});
+      else segments(std::integral_constant<int, 32>{}, std::false_type{});
+    }
+  } else if (KP == 4) {
     if (active) tree_and_stream(std::integral_constant<int, 16>{}, std::true_type{});
     else tree_and_stream(std::integral_constant<int, 16>{}, std::false_type{});
   } else {
@@ -1548,63 +1512,39 @@ __global__ void __launch_bounds__(kMaxTreeSplit) mask_words_kernel(Params p, uin
 }
 
 // ========================================================== suffix kernel
-// One workgroup per (sequence, KV head, row pass); D/4 lanes per row, reading
-// q and the tree rows from global memory.  Writes normalised o and natural-log
-// lse of the tree piece.
+// The tree piece of the split path: one workgroup per (sequence, KV head,
+// row pass), the item's rows against every tree node in 64-node segments
+// under the precomputed mask words, on the MFMA path of the prefix kernel.
+// Writes normalised o and natural-log lse (fp32).  Invalid tree offsets
+// leave the sequence's rows unwritten.
+// [draft-token piece that needs the tree mask: pith.science review,
+// "What carries the argument"]
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) suffix_kernel(Params p) {
-  constexpr int L4 = D / 4;
-  constexpr int NSLOT = kThreads / L4;
+__global__ void __launch_bounds__(kAttnThreads, 1) suffix_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
+  __shared__ SmemMisc sm;
+  unsigned char* ring = reinterpret_cast<unsigned char*>(dyn);
   const int grp = blockIdx.x;
-  const int rp = grp % p.rp_max;
+  Item it;
+  it.rp = grp % p.rp_max;
   const int bg = grp / p.rp_max;
-  const int g = bg % p.hkv;
-  const int b = bg / p.hkv;
-  const int o0 = p.tree_offsets[b];
-  const int o1 = p.tree_offsets[b + 1];
+  it.g = bg % p.hkv;
+  it.b = bg / p.hkv;
+  it.s = 0;
+  it.grp = grp;
+  it.chunk = kBlock;
+  const int o0 = p.tree_offsets[it.b];
+  const int o1 = p.tree_offsets[it.b + 1];
   const int Tn = o1 - o0;
-  if (!(o0 >= 0 && o1 >= o0 && o1 <= p.total_nodes && Tn <= p.max_tree)) return;
-  const int G = p.group;
-  const int R = Tn * G;
-  const int rlo = rp * kRowsPerPass;
-  if (rlo >= R) return;
-  const int rcount = min(kRowsPerPass, R - rlo);
-  const int rs = threadIdx.x / L4;
-  const int d4 = threadIdx.x % L4;
-  for (int r0 = 0; r0 < rcount; r0 += NSLOT) {
-    const int r = r0 + rs;
-    if (r >= rcount) break;
-    const int rr = rlo + r;
-    const size_t orow = size_t(o0 + rr / G) * p.hq + g * G + rr % G;
-    const T* kt = static_cast<const T*>(p.k_tree) + (size_t(o0) * p.hkv + g) * D;
-    const T* vt = static_cast<const T*>(p.v_tree) + (size_t(o0) * p.hkv + g) * D;
-    // the tree in segments of 64 keys, one mask word each, folded by their
-    // log-sum-exps (base 2)
-    float m = -INFINITY, l = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int seg = 0; seg * 64 < Tn; ++seg) {
-      const uint64_t word = p.mask_in[size_t(o0 + rr / G) * p.mask_words + seg];
-      const size_t koff = size_t(seg) * 64 * p.hkv * D;
-      TreeSrc<T, D> src{static_cast<const T*>(p.q) + orow * D, kt + koff, vt + koff, p.hkv * D,
-                        p.hkv * D, false};
-      float ms, ls;
-      float4 os;
-      tree_row<T, D>(src, min(64, Tn - seg * 64), d4, word, p.scale_log2, ms, ls, os);
-      if (ms == -INFINITY) continue;
-      const float mn = fmaxf(m, ms);
-      const float a = m == -INFINITY ? 0.f : exp2_fast(m - mn);
-      const float c = exp2_fast(ms - mn);
-      l = l * a + ls * c;
-      o = make_float4(o.x * a + os.x * c, o.y * a + os.y * c, o.z * a + os.z * c,
-                      o.w * a + os.w * c);
-      m = mn;
-    }
-    const bool empty = m == -INFINITY;
-    const float inv = empty ? 0.f : 1.f / l;
-    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * D + 4 * d4) =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    if (d4 == 0) p.lse_out[orow] = empty ? -INFINITY : (m + __log2f(l)) * kLn2;
-  }
+  if (!(o0 >= 0 && o1 > o0 && o1 <= p.total_nodes && Tn <= p.max_tree)) return;
+  it.si.off = o0;
+  it.si.T = Tn;
+  it.si.P = 0;
+  it.si.S = 1;
+  it.si.RP = cdiv(Tn * p.group, kRowsPerPass);
+  it.si.items = p.hkv * it.si.RP;
+  if (it.rp >= it.si.RP) return;
+  process_item<T, D, false, true>(p, ring, ring, sm, it, grp, false);
 }
 
 // =========================================================== merge kernel
