@@ -92,6 +92,7 @@ struct Params {
   int tree_in_cache;         // 1: tree K/V rows are cache positions P .. P+T-1 (k_tree unused)
   int single;                // 1: one sequence, items numbered without a table
   int single_items;          // item count of a one-sequence launch
+  int xcd_major;             // 1: first-round items numbered XCD-major (see attn_kernel)
   int first_round;           // workgroups in the grid
   int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
   int ns;                    // KV ring slots in LDS, 1..kMaxRingSlots

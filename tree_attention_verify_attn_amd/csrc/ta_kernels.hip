@@ -1415,6 +1415,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   // numbers are adjacent to its own, and a group has no more chunks than the
   // grid has workgroups, so every awaited chunk is taken and finished.
   int li = int(blockIdx.x);
+  if (p.xcd_major && li < items) li = (li % 8) * (items / 8) + li / 8;
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
     const Item it = p.single ? decode_single(p, li) : decode_item(p, chunk, cum, ot, pl, perm, li);
