@@ -327,9 +327,9 @@ def main() -> int:
 
     log(f"building workload cfg{args.config}")
     inp = make_config(args.config)
-    if inp.max_tree_nodes > 64 and args.entry != "split":
-        log("trees of more than 64 nodes run on the split path")
-        args.entry = "split"
+    if inp.max_tree_nodes > 64 and args.entry == "incache":
+        log("in-cache tree rows are for trees of up to 64 nodes; using the fused verify")
+        args.entry = "verify"
     if args.entry == "incache":
         inp = incache_layout(inp)
     nbytes = algorithmic_bytes(inp)

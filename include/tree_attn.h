@@ -98,9 +98,10 @@ typedef struct {
   int32_t head_dim;           /* D in {64, 128} */
   int32_t block_size;         /* tokens per KV block; must be 64 */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
-  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size: 1..64 for the
-                                 fused verify, acceptance and commit; 1..256 for the split
-                                 path (build_mask, prefix, suffix, merge) */
+  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size: 1..256 for the
+                                 fused verify and the split path (build_mask, prefix,
+                                 suffix, merge); 1..64 for the in-cache verify,
+                                 acceptance and commit */
   int32_t max_prefix_len;     /* upper bound on prefix_lens[b], 0..64*max_blocks_per_seq */
   int32_t total_tree_nodes;   /* N = tree_offsets[B] */
   int32_t num_blocks;         /* pool size: valid block ids are [0, num_blocks) */
@@ -173,8 +174,10 @@ ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype,
 
 /* Fused verify: prefix pass + mask build + suffix pass + merge in one kernel
  * launch.  Writes out (shape->dtype) and lse_out (fp32, may be NULL).  Trees
- * of up to 64 nodes (max_tree_nodes <= 64, else TA_ERR_UNSUPPORTED); larger
- * trees take the split path.
+ * of up to 256 nodes (max_tree_nodes <= 256, else TA_ERR_UNSUPPORTED).  Up to
+ * 64 nodes the tree rows sit in LDS beside the KV ring; larger trees stream
+ * through the ring in 64-node segments after the last chunk's KV blocks,
+ * under mask words the kernel builds in LDS.
  * [pith.science review, "What carries the argument"] */
 ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* block_table,

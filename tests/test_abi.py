@@ -124,13 +124,15 @@ def test_split_tokens_bounds():
 
 
 @pytest.mark.parametrize("T", [65, 200, 256])
-def test_large_trees_split_path_only(T):
-    # trees of 65..256 nodes: the split path sizes a workspace; the fused verify,
-    # acceptance and commit refuse them before touching any pointer
+def test_large_trees_verify_and_split_only(T):
+    # trees of 65..256 nodes: the split path and the fused verify size a
+    # workspace (the verify gets as far as the workspace check: a null one is
+    # refused, not the shape); in-cache verify, acceptance and commit refuse
+    # the shape before touching any pointer
     s = shape(max_tree_nodes=T, total_tree_nodes=T)
     assert ta.workspace_size(s) > 0
     assert ta.split_tokens(s) > 0
     lib = load()
-    assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None) == 2
+    assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), None, 1 << 40, None) == 4
     assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), FAKE, 1 << 40, None) == 2
     assert lib.tree_attn_accept_greedy(ctypes.byref(s), *([FAKE] * 7), FAKE, 1 << 40, None) == 2

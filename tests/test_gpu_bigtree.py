@@ -1,13 +1,14 @@
-"""GPU parity for trees of more than 64 nodes (up to 256) on the split path:
-multi-word masks bit for bit, and mask + prefix + suffix + merge against the
-fp64 oracle.  Also the draft-side shape: short prefixes under large trees
-(multi-round drafting attends with the same kernels)."""
+"""GPU parity for trees of more than 64 nodes (up to 256): multi-word masks
+bit for bit; mask + prefix + suffix + merge (split path) and the fused verify
+against the fp64 oracle.  Also the draft-side shape: short prefixes under
+large trees (multi-round drafting attends with the same kernels)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, assert_close_lse, host, run_split, say, to_device, tolerances
+from gpu_util import (assert_close, assert_close_lse, host, run_split, run_verify, say,
+                      to_device, tolerances)
 from helpers import random_tree
 from workloads import make_inputs
 
@@ -87,3 +88,72 @@ def test_large_tree_bad_parent_flagged():
     assert not got[:200].any()          # the bad tree's words are zero
     want = oracle.build_masks_words(inp, 4)
     np.testing.assert_array_equal(got[200:], want[200:])   # the others are intact
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_fused_verify_large_trees_matches_oracle(dtype, D):
+    # trees of 65..256 nodes in one launch: the last chunk of each group runs
+    # the tree's 64-node segments after its KV blocks
+    import tree_attention_verify_attn_amd as ta
+    trees = _trees(5)
+    inp = _big(95, trees, [300, 0, 1000, 65, 7], dtype=dtype, D=D)
+    d = to_device(inp, max_tree_nodes=256)
+    say(f"fused verify, trees up to 256 nodes, {dtype} D={D}")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(out), o_want, tol_o, "fused big-tree o")
+    assert_close_lse(host(lse), l_want, tol_l, "fused big-tree lse")
+
+
+def test_fused_verify_large_tree_one_sequence_split_chunks():
+    # one sequence (numbered without a table), a 256-node tree over a
+    # 4000-token prefix cut into many chunks; small trees mixed in are covered
+    # by the test above
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(96)
+    inp = _big(96, [random_tree(rng, 256)], [4000], Hq=8, Hkv=2)
+    d = to_device(inp, max_tree_nodes=256, split_tokens=256)
+    say("fused verify, one sequence, 256-node tree, 16 chunks")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    assert_close(host(out), o_want, 2e-2, "one-sequence big-tree o")
+    assert_close_lse(host(lse), l_want, 1e-3, "one-sequence big-tree lse")
+
+
+def test_fused_verify_draft_side_matches_split():
+    # the draft-side shape through the fused verify, against the oracle and
+    # the split path
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(97)
+    trees = [random_tree(rng, 128) for _ in range(8)]
+    lens = [int(x) for x in rng.integers(16, 101, size=8)]
+    inp = make_inputs(dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      prefix_lens=lens, trees=trees, rng=rng)
+    d = to_device(inp, max_tree_nodes=128)
+    say("fused verify, draft-side shape")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    assert_close(host(out), o_want, 2e-2, "fused draft-side o")
+    assert_close_lse(host(lse), l_want, 1e-3, "fused draft-side lse")
+    out2, lse2, _ = run_split(d)
+    assert_close(host(out), host(out2), 2e-2, "fused vs split o")
+
+
+def test_fused_verify_large_tree_bad_parent_flagged():
+    import tree_attention_verify_attn_amd as ta
+    trees = _trees(6)
+    inp = _big(98, trees, [100] * len(trees))
+    d = to_device(inp, max_tree_nodes=256)
+    d.parents[150] = 170       # a later node of the 200-node tree
+    say("fused verify, large tree with a bad parent")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 3
+    # every other sequence is still right
+    o_want, l_want, _ = oracle.verify(inp)
+    off = inp.tree_offsets
+    rows = slice(int(off[1]), int(off[-1]))
+    assert_close(host(out)[rows], o_want[rows], 2e-2, "other sequences o")

@@ -85,8 +85,14 @@ int group_of(const ta_shape* s) { return s->num_q_heads / s->num_kv_heads; }
 const void* attn_kernel_ptr(const ta_shape* s, bool fused);
 
 // LDS bytes for the tree K rows (the same again for tree V) of the fused kernel.
+// Trees of more than 64 nodes stage no rows there (their segments go through
+// the ring); the area then holds the nodes' mask words and links instead.
 int tree_lds_half(const ta_shape* s, bool fused) {
   if (!fused) return 0;
+  if (s->max_tree_nodes > kMaxTree) {
+    const int bytes = kMaxTreeSplit * (kMaxTreeSplit / 64) * 8 + kMaxTreeSplit * 4;
+    return 1024 * cdiv(cdiv(bytes, 2), 1024);
+  }
   const int rowb = s->head_dim * (s->dtype == TA_DTYPE_BF16 ? 2 : 4);
   return 1024 * cdiv(s->max_tree_nodes * rowb, 1024);
 }
@@ -241,18 +247,26 @@ int launch_status() {
   return e == hipSuccess ? kOk : kErrHip;
 }
 
+// Fused launches for trees of more than kMaxTree nodes run their own kernel
+// (the tree's segments through the ring), so that the common fused kernel
+// keeps its registers.
+bool big_fused(const ta_shape* s, bool fused) { return fused && s->max_tree_nodes > kMaxTree; }
+
 template <typename T, int D, bool FUSED>
-const void* attn_ptr() {
+const void* attn_ptr(bool big) {
+  if constexpr (FUSED)
+    if (big) return reinterpret_cast<const void*>(&attn_kernel<T, D, true, true>);
   return reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED>);
 }
 
 const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
+  const bool big = big_fused(s, fused);
   if (s->dtype == TA_DTYPE_BF16) {
-    if (s->head_dim == 128) return fused ? attn_ptr<uint16_t, 128, true>() : attn_ptr<uint16_t, 128, false>();
-    return fused ? attn_ptr<uint16_t, 64, true>() : attn_ptr<uint16_t, 64, false>();
+    if (s->head_dim == 128) return fused ? attn_ptr<uint16_t, 128, true>(big) : attn_ptr<uint16_t, 128, false>(big);
+    return fused ? attn_ptr<uint16_t, 64, true>(big) : attn_ptr<uint16_t, 64, false>(big);
   }
-  if (s->head_dim == 128) return fused ? attn_ptr<float, 128, true>() : attn_ptr<float, 128, false>();
-  return fused ? attn_ptr<float, 64, true>() : attn_ptr<float, 64, false>();
+  if (s->head_dim == 128) return fused ? attn_ptr<float, 128, true>(big) : attn_ptr<float, 128, false>(big);
+  return fused ? attn_ptr<float, 64, true>(big) : attn_ptr<float, 64, false>(big);
 }
 
 // The split path's tree piece: one workgroup per (sequence, KV head, row
@@ -276,7 +290,8 @@ int launch_suffix(const ta_shape* s, Params p, unsigned grid, hipStream_t stream
 
 template <typename T, int D, bool FUSED>
 int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stream) {
-  const void* kern = attn_ptr<T, D, FUSED>();
+  const bool big = big_fused(s, FUSED);
+  const void* kern = attn_ptr<T, D, FUSED>(big);
   p.tree_lds_half = tree_lds_half(s, FUSED);
   p.ns = ring_slots(s, FUSED);
   if (p.ns < 1) return kErrUnsupported;  // tree rows + sequence table leave no room for the ring
@@ -301,6 +316,12 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
     const int RP = cdiv(s->max_tree_nodes * group_of(s), kRowsPerPass);
     p.xcd_major = p.single && RP > 1 && p.single_items % 8 == 0 && p.single_items <= first ? 1 : 0;
   }
+  if constexpr (FUSED)
+    if (big) {
+      hipLaunchKernelGGL((attn_kernel<T, D, true, true>), dim3(unsigned(first)), dim3(kAttnThreads),
+                         dyn, stream, p);
+      return launch_status();
+    }
   hipLaunchKernelGGL((attn_kernel<T, D, FUSED>), dim3(unsigned(first)), dim3(kAttnThreads),
                      dyn, stream, p);
   return launch_status();
@@ -332,17 +353,14 @@ extern "C" {
 
 size_t tree_attn_workspace_size(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
-  // the fused kernel serves trees of up to 64 nodes only
-  const size_t a = shape->max_tree_nodes <= kMaxTree
-                       ? layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true)).total
-                       : 0;
+  const size_t a = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true)).total;
   const size_t b = layout_for(shape, choose_chunk(shape, false), auto_cap(shape, false)).total;
   return a > b ? a : b;
 }
 
 int32_t tree_attn_split_tokens(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
-  return choose_chunk(shape, shape->max_tree_nodes <= kMaxTree);
+  return choose_chunk(shape, true);
 }
 
 ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -466,7 +484,6 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
                            float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!prefix_lens || !tree_offsets || !block_table) return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !parents || !out))
     return TA_ERR_INVALID_ARG;

@@ -409,8 +409,17 @@ struct Geo {
   static_assert(NSMAX * 2 * KI < 64, "vmcnt range");
 };
 
+// words of SmemMisc::hid: landing places of the hidden loads of an item's
+// first round trip
+constexpr int kHidSense = 0;                  // the group's sense word (thread 0)
+constexpr int kHidOff = 1;                    // tree_offsets[0], [1] (wave 0, lanes 0 and 1)
+constexpr int kHidP = 4;                      // the prefix length, per wave
+constexpr int kHidBlk = kHidP + kAttnWaves;   // two tree-region block ids, per wave
+constexpr int kHidWords = kHidBlk + 2 * kAttnWaves;
+
 struct SmemMisc {
   uint64_t mask[kMaxTree];
+  int hid[kHidWords];
   int scratch[kAttnThreads];
   int bcast[4];
   float half_m[kMaxTree];  // running max / sum of the upper key half, per row
@@ -512,25 +521,22 @@ __device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char*
   for (int i = 0; i < Gm::KI; ++i) lds_dma16_tile(g, Gm::BLKB, off[i], lds + (w * Gm::KI + i) * 1024);
 }
 
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-// A 32-bit global load hidden from the compiler.  Its value is read only
-// after the caller's own wait and `settle`, so the compiler cannot pull a
-// wait for it (or its move to a scalar register) in front of the loads
-// issued after it.
+// A 32-bit global load hidden from the compiler, landing in LDS (lane i's
+// word at lds_base + 4 i, lds_base wave-uniform) like the block transfers.
+// Its value is read from LDS after the caller's own wait, so no compiler wait
+// for it lands in front of the loads issued after it; and no register is
+// written behind the compiler's back (a register the compiler spilled while
+// such a load was in flight would keep its old value).
 // kCoherentLoad reads past this XCD's L2, as an agent-scope load does.
 template <bool kCoherentLoad = false>
-__device__ __forceinline__ int hidden_load(const int* ptr) {
-  int v;
+__device__ __forceinline__ void hidden_load(const int* ptr, int* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)));
   if constexpr (kCoherentLoad)
-    asm volatile("global_load_dword %0, %1, off sc1" : "=v"(v) : "v"(ptr) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off sc1" ::"s"(m0), "v"(ptr) : "memory");
   else
-    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(ptr) : "memory");
-  return v;
-}
-// Ties a hidden load's register to this point (after an s_waitcnt).
-__device__ __forceinline__ int settle(int v) {
-  asm volatile("" : "+v"(v)::"memory");
-  return v;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(ptr) : "memory");
+#endif
 }
 
 template <int n>
@@ -608,7 +614,7 @@ constexpr float kRescaleSlack = 8.f;
 // SUFFIX: the tree piece of the split path on its own -- no prefix, the tree
 // keys streamed through the ring in segments of 64 nodes, each under its
 // word of the precomputed ancestor-or-self mask (p.mask_in), fp32 outputs.
-template <typename T, int D, bool FUSED, bool SUFFIX = false>
+template <typename T, int D, bool FUSED, bool SUFFIX = false, bool BIG = false>
 __device__ __forceinline__ void process_item(const Params& p, unsigned char* ring,
                                              unsigned char* tree_lds,
                                              SmemMisc& sm, const Item& it, int slot_index,
@@ -664,9 +670,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // a wait the compiler would otherwise place before reusing registers of the
   // previous item lands here, not between the loads of this trip
   wait_vm<0>();
-  int sense_read = 0;  // hidden: a compiler wait for it would stall the loads below
+  // hidden (sm.hid): a compiler wait for it would stall the loads below
   if constexpr (!SUFFIX)
-    if (tid == 0) sense_read = hidden_load<true>(reinterpret_cast<const int*>(sense));
+    if (tid == 0) hidden_load<true>(reinterpret_cast<const int*>(sense), &sm.hid[kHidSense]);
   uint4 qv[QCH];
   {
     const int r = 16 * rt + lr;
@@ -685,7 +691,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // the parent array (the tree chunk needs it; in a one-sequence launch which
   // chunk that is is known only with the prefix length, so every chunk reads it)
   int par = -1;
-  if (FUSED && w == 0 && (need_p || it.s == si.S - 1)) par = p.parents[si.off + min(lane, si.T - 1)];
+  // (more than 64 nodes: thread i reads node i's parent)
+  if (FUSED && (BIG ? tid < kMaxTreeSplit : w == 0) && (need_p || it.s == si.S - 1))
+    par = p.parents[si.off + min(BIG ? tid : lane, si.T - 1)];
   // tree rows kept in the cache right after the prefix (positions P .. P+T-1,
   // at most two blocks).  The region starts inside this chunk's block range
   // or right after it, so two more lanes of the block-id load below cover its
@@ -695,17 +703,16 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // table, so P is known here).
   const int cpb = it.chunk / kBlock;  // blocks per chunk
   const bool extra_lanes = FUSED && p.tree_in_cache && cpb + 2 <= 64;
-  int tree_blk = 0;
-  if (FUSED && p.tree_in_cache && !extra_lanes && it.s == si.S - 1 && lane < 2)
-    tree_blk = hidden_load(p.block_table + size_t(it.b) * p.max_blocks +
-                           min(si.P / kBlock + lane, p.max_blocks - 1));
+  const bool tree_blk_here = FUSED && p.tree_in_cache && !extra_lanes && it.s == si.S - 1;
+  if (tree_blk_here && lane < 2)
+    hidden_load(p.block_table + size_t(it.b) * p.max_blocks + min(si.P / kBlock + lane, p.max_blocks - 1),
+                &sm.hid[kHidBlk + 2 * w]);
   // one-sequence numbering: the prefix length, and (first item only) the two
   // tree offsets, which must be 0 and N
   const bool first_of_launch = it.s == 0 && it.g == 0 && it.rp == 0;
-  int p_read = 0, toff = 0;
   if (need_p) {
-    p_read = hidden_load(p.prefix_lens);
-    if (first_of_launch && w == 0) toff = hidden_load(p.tree_offsets + (lane & 1));
+    if (lane == 0) hidden_load(p.prefix_lens, &sm.hid[kHidP + w]);
+    if (first_of_launch && w == 0 && lane < 2) hidden_load(p.tree_offsets + lane, &sm.hid[kHidOff]);
   }
   int my_id = -1;
   if constexpr (!SUFFIX) {
@@ -726,11 +733,11 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     }
   }
   wait_vm<0>();
-  const unsigned sense0 = unsigned(settle(sense_read));
-  tree_blk = settle(tree_blk);
+  const unsigned sense0 = tid == 0 ? unsigned(sm.hid[kHidSense]) : 0u;  // used by thread 0 only
+  const int tree_blk = tree_blk_here && lane < 2 ? sm.hid[kHidBlk + 2 * w + lane] : 0;
   if (need_p) {
-    p_read = __builtin_amdgcn_readfirstlane(settle(p_read));  // the same in every lane
-    toff = settle(toff);
+    const int p_read = __builtin_amdgcn_readfirstlane(sm.hid[kHidP + w]);  // the same in every lane
+    const int toff = first_of_launch && w == 0 && lane < 2 ? sm.hid[kHidOff + lane] : 0;
     if (first_of_launch && w == 0 && lane < 2 && toff != (lane == 0 ? 0 : si.T))
       set_error(p.hdr, kErrBadTree);
     const bool p_ok = p_read >= 0 && p_read <= p.max_prefix;
@@ -744,6 +751,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   const int nblk = cdiv(ntok, kBlock);
   const int S = si.S;
   const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
+  // trees of more than 64 nodes (fused): their 64-node segments follow the
+  // chunk's KV blocks through the ring, under mask words built in LDS
+  constexpr bool big = FUSED && BIG;
 
   // ---- tree rows (fused, last chunk only): DMA into LDS, issued before the KV
   // blocks so that waiting for them does not wait for the blocks.  Every
@@ -751,8 +761,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // are finite.
   unsigned char* tk = tree_lds;
   unsigned char* tv = tree_lds + p.tree_lds_half;
-  const int tree_rows = SUFFIX ? kBlock : p.tree_lds_half / ROWB;  // staged rows (>= tree size)
-  if (with_tree) {
+  const int tree_rows = (SUFFIX || big) ? kBlock : p.tree_lds_half / ROWB;  // staged rows (>= tree size)
+  if (with_tree && !big) {
     const int Tn = si.T;
     const int ninstr = p.tree_lds_half / 1024;
     // in-cache rows: the region's two block ids (checked; a bad one is
@@ -818,11 +828,71 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot, doff);
     dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB, doff);
   };
-  for (int j = 0; j < NS && j < nblk; ++j) issue(j);
+  // tree segments (64 nodes each) go through the ring like KV blocks, after
+  // the item's KV blocks (ring unit nblk + segment): in the split path's
+  // suffix mode, and in the fused kernel's last chunk for trees of more than
+  // 64 nodes.  Each stages the segment's rows, clamped to the last node,
+  // gathered from the [node, KV head, D] tree tensors: KI transfers per wave
+  // and tensor, like a KV block.
+  const int nseg = (SUFFIX || (with_tree && big)) ? cdiv(si.T, kBlock) : 0;
+  const int ntot = nblk + nseg;  // ring units of the item
+  auto stage = [&](int j) {
+    const int sg = j - nblk;
+    unsigned char* sk = ring + (j % NS) * SLOTB;
+    for (int m = w; m < BLKB / 1024; m += kAttnWaves) {
+      const int u = m * 64 + lane;
+      const int t = min(kBlock * sg + u / KCH, si.T - 1);
+      const int pc = u % KCH;
+      const int c = pc ^ ((u / KCH) & SWZ);
+      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff) + c * 16,
+                sk + m * 1024);
+      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff) + c * 16,
+                sk + BLKB + m * 1024);
+    }
+  };
+  auto issue_any = [&](int j) {
+    if (j < nblk) issue(j);
+    else stage(j);
+  };
+  for (int j = 0; j < NS && j < ntot; ++j) issue_any(j);
 
   // ---- tree staging: wait for the tree DMA (older than the blocks), then the
   // tree mask by pointer jumping (as in tree_mask_wave)
-  if (with_tree) {
+  if (with_tree && big) {
+    // node i (thread i) keeps its ancestor-or-self set in kSegMax words and a
+    // link to an ancestor; eight rounds through LDS OR in the linked node's
+    // set and follow its link.  Words of node i end at bw[i * kSegMax ..].
+    uint64_t* bw = reinterpret_cast<uint64_t*>(tree_lds);
+    int* bup = reinterpret_cast<int*>(tree_lds + kMaxTreeSplit * kSegMax * sizeof(uint64_t));
+    const int Tn = si.T;
+    const bool node = tid < kMaxTreeSplit;
+    const bool bad_i = node && tid < Tn && !(par == -1 || (par >= 0 && par < tid));
+    int up = (node && tid < Tn && !bad_i) ? par : -1;
+    uint64_t anc[kSegMax];
+#pragma unroll
+    for (int x = 0; x < kSegMax; ++x)
+      anc[x] = (node && tid < Tn && tid / 64 == x) ? (uint64_t(1) << (tid % 64)) : 0;
+    for (int round = 0; round < 8; ++round) {
+      if (node) {
+#pragma unroll
+        for (int x = 0; x < kSegMax; ++x) bw[tid * kSegMax + x] = anc[x];
+        bup[tid] = up;
+      }
+      __syncthreads();
+      if (node && up >= 0) {
+#pragma unroll
+        for (int x = 0; x < kSegMax; ++x) anc[x] |= bw[up * kSegMax + x];
+        up = bup[up];
+      }
+      __syncthreads();
+    }
+    if (node) {
+#pragma unroll
+      for (int x = 0; x < kSegMax; ++x) bw[tid * kSegMax + x] = anc[x];
+    }
+    if (__syncthreads_or(bad_i) && tid == 0 && it.g == 0 && it.rp == 0) set_error(p.hdr, kErrBadTree);
+  } else if (with_tree) {
     wait_blocks<KI, NSMAX>(min(nblk, NS));
     if (w == 0) {
       const int Tn = si.T;
@@ -876,7 +946,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     uint64_t word = 0;
     if constexpr (kTree) {
       const int r = 16 * rt + lr;
-      word = SUFFIX ? tword : (r < rcount ? sm.mask[(rlo + r) / G] : 0);
+      word = (SUFFIX || big) ? tword : (r < rcount ? sm.mask[(rlo + r) / G] : 0);
     }
     // every LDS read of the block is issued before the first MFMA
     uint4 kf[NA][QCH];
@@ -1030,7 +1100,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     constexpr bool kMasked = decltype(mask_tag)::value;
     for (int j = j0; j < j1; ++j) {
       unsigned char* slot = ring + (j % NS) * SLOTB;
-      wait_blocks<KI, NSMAX>(min(NS - 1, nblk - 1 - j));
+      wait_blocks<KI, NSMAX>(min(NS - 1, ntot - 1 - j));
       raw_barrier();
       int nv = kBlock;
       if constexpr (kMasked) {
@@ -1043,14 +1113,30 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       if constexpr (decltype(act_tag)::value)
         compute(std::false_type{}, ks_tag, mask_tag, slot, slot + BLKB, nv, 0);
       raw_barrier();
-      if (j + NS < nblk) issue(j + NS);
+      if (j + NS < ntot) issue_any(j + NS);
     }
   };
   // the tree piece (while the first KV blocks are still in flight), then the
   // full blocks without the per-key mask and a partial last block with it;
   // a chunk with a bad block id takes the masked loop throughout
+  // the tree's segments after the KV blocks (trees of more than 64 nodes),
+  // each under its mask word from LDS
+  auto big_segments = [&](auto ks_tag, auto act_tag) {
+    const uint64_t* bw = reinterpret_cast<const uint64_t*>(tree_lds);
+    for (int j = nblk; j < ntot; ++j) {
+      unsigned char* slot = ring + (j % NS) * SLOTB;
+      wait_blocks<KI, NSMAX>(min(NS - 1, ntot - 1 - j));
+      raw_barrier();
+      const int r = 16 * rt + lr;
+      const uint64_t word = r < rcount ? bw[((rlo + r) / G) * kSegMax + (j - nblk)] : 0;
+      if constexpr (decltype(act_tag)::value)
+        compute(std::true_type{}, ks_tag, std::true_type{}, slot, slot + BLKB, 0, word);
+      raw_barrier();
+      if (j + NS < ntot) issue_any(j + NS);
+    }
+  };
   auto tree_and_stream = [&](auto ks_tag, auto act_tag) {
-    if (with_tree) {
+    if (with_tree && !big) {
       raw_barrier();  // staged rows of every wave and the mask words are in LDS
       if constexpr (decltype(act_tag)::value)
         compute(std::true_type{}, ks_tag, std::true_type{}, tk, tv, 0, 0);
@@ -1062,24 +1148,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       stream(ks_tag, std::false_type{}, act_tag, 0, nfull);
       stream(ks_tag, std::true_type{}, act_tag, nfull, nblk);
     }
-  };
-  // suffix: the tree's 64-node segments go through the ring like KV blocks
-  // (the rows of the segment, clamped to the last node, gathered from the
-  // [node, KV head, D] tree tensors: KI transfers per wave and tensor)
-  const int nseg = SUFFIX ? cdiv(si.T, kBlock) : 0;
-  auto stage = [&](int sg) {
-    unsigned char* sk = ring + (sg % NS) * SLOTB;
-    for (int m = w; m < BLKB / 1024; m += kAttnWaves) {
-      const int u = m * 64 + lane;
-      const int t = min(kBlock * sg + u / KCH, si.T - 1);
-      const int pc = u % KCH;
-      const int c = pc ^ ((u / KCH) & SWZ);
-      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
-      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff) + c * 16,
-                sk + m * 1024);
-      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff) + c * 16,
-                sk + BLKB + m * 1024);
-    }
+    if (with_tree && big) big_segments(ks_tag, act_tag);
   };
   auto segments = [&](auto ks_tag, auto act_tag) {
     // unrolled, so that segw is indexed by constants and stays in registers
@@ -1092,11 +1161,10 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       if constexpr (decltype(act_tag)::value)
         compute(std::true_type{}, ks_tag, std::true_type{}, slot, slot + BLKB, 0, segw[sg]);
       raw_barrier();
-      if (sg + NS < nseg) stage(sg + NS);
+      if (sg + NS < nseg) issue_any(sg + NS);
     }
   };
   if constexpr (SUFFIX) {
-    for (int sg = 0; sg < NS && sg < nseg; ++sg) stage(sg);
     if (KP == 4) {
       if (active) segments(std::integral_constant<int, 16>{}, std::true_type{});
       else segments(std::integral_constant<int, 16>{}, std::false_type{});
@@ -1386,7 +1454,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
 }
 
-template <typename T, int D, bool FUSED>
+template <typename T, int D, bool FUSED, bool BIG = false>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   using Gm = Geo<T, D>;
   // dynamic LDS: the KV ring (ns slots), the tree rows (K then V), the table
@@ -1419,7 +1487,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
     const Item it = p.single ? decode_single(p, li) : decode_item(p, chunk, cum, ot, pl, perm, li);
-    process_item<T, D, FUSED>(p, ring, tree_lds, sm, it, li, tickets);
+    process_item<T, D, FUSED, false, BIG>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
     if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket, 1u));
