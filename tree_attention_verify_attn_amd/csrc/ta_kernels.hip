@@ -426,11 +426,30 @@ struct SmemMisc {
   float half_l[kMaxTree];
 };
 
+// XOR key of row t's 16-byte chunks in a swizzled row-major tile: logical
+// chunk c sits at physical chunk c ^ swz_key(t).  For bf16 rows of 16 chunks
+// the key is a bit permutation of t (bits 0-2 move up one, bit 0 becomes
+// bit 2 ^ bit 3), so that
+//  - the K reads (16 consecutive rows at one chunk, 16 bytes a lane) hit 16
+//    distinct chunks, also any 8 aligned rows 8 distinct chunks mod 8, and
+//  - the transposing V reads (per 32 lanes: 8 aligned rows, two adjacent
+//    chunks, 8 bytes a lane) cover all 16 chunks once: no two lanes of a pass
+//    share a bank.  The plain key t & 15 put two lanes on each bank there.
+// Other tiles keep the plain key.
+template <typename T, int D>
+__device__ __forceinline__ int swz_key(int t) {
+  using Gm = Geo<T, D>;
+  if constexpr (sizeof(T) == 2 && Gm::KCH == 16)
+    return (((t >> 2) ^ (t >> 3)) & 1) | ((t & 7) << 1);
+  else
+    return t & Gm::SWZ;
+}
+
 // byte offset of logical 16-byte chunk c of row t in a swizzled row-major tile
 template <typename T, int D>
 __device__ __forceinline__ int swz_off(int t, int c) {
   using Gm = Geo<T, D>;
-  return t * Gm::ROWB + ((c ^ (t & Gm::SWZ)) << 4);
+  return t * Gm::ROWB + ((c ^ swz_key<T, D>(t)) << 4);
 }
 
 // Direct global -> LDS transfers (16 bytes per lane, landing at lds_base + 16 *
@@ -474,7 +493,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* a) {
 
 // Source byte offsets, within one 64-token K or V tile, of the 16-byte chunks
 // this lane moves: instruction i of wave w fills LDS chunks (w KI + i) 64 +
-// lane, i.e. row t, physical chunk pc, which holds logical chunk pc ^ (t & SWZ).
+// lane, i.e. row t, physical chunk pc, which holds logical chunk pc ^ swz_key(t).
 template <typename T, int D>
 __device__ __forceinline__ void dma_offsets(uint32_t* off) {
   using Gm = Geo<T, D>;
@@ -485,7 +504,7 @@ __device__ __forceinline__ void dma_offsets(uint32_t* off) {
     const int u = (w * Gm::KI + i) * 64 + lane;
     const int t = u / Gm::KCH;
     const int pc = u % Gm::KCH;
-    off[i] = uint32_t(t * Gm::ROWB + ((pc ^ (t & Gm::SWZ)) << 4));
+    off[i] = uint32_t(t * Gm::ROWB + ((pc ^ swz_key<T, D>(t)) << 4));
   }
 }
 
@@ -620,7 +639,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
                                              SmemMisc& sm, const Item& it, int slot_index,
                                              bool solo_combine) {
   using Gm = Geo<T, D>;
-  constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, SWZ = Gm::SWZ, BLKB = Gm::BLKB, KI = Gm::KI,
+  constexpr int ROWB = Gm::ROWB, KCH = Gm::KCH, BLKB = Gm::BLKB, KI = Gm::KI,
                 QCH = Gm::QCH, DT = Gm::DT, NSMAX = Gm::NSMAX;
   const int NS = p.ns;  // ring slots of this launch, 1..NSMAX
   constexpr bool kBf16 = sizeof(T) == 2;
@@ -790,7 +809,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       const int u = m * 64 + lane;
       const int t = min(u / KCH, Tn - 1);
       const int pc = u % KCH;
-      const int c = pc ^ ((u / KCH) & SWZ);
+      const int c = pc ^ swz_key<T, D>(u / KCH);
       size_t roff;
       const T* kb;
       const T* vb;
@@ -843,7 +862,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       const int u = m * 64 + lane;
       const int t = min(kBlock * sg + u / KCH, si.T - 1);
       const int pc = u % KCH;
-      const int c = pc ^ ((u / KCH) & SWZ);
+      const int c = pc ^ swz_key<T, D>(u / KCH);
       const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
       lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff) + c * 16,
                 sk + m * 1024);
@@ -972,7 +991,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
         for (int h = 0; h < NA; ++h) {
           const int row = krow(kbase + 16 * h + 4 * kq + (L >> 2));
           const int cb = 32 * dt + 8 * (L & 3);  // byte column
-          half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
+          half[h] = lds_read_tr16(vb + row * ROWB + (((cb >> 4) ^ swz_key<T, D>(row)) << 4) + (cb & 15));
         }
         if constexpr (NA == 2) vf[dt] = make_uint4(half[0].x, half[0].y, half[1].x, half[1].y);
         else vf[dt] = make_uint4(half[0].x, half[0].y, 0u, 0u);
@@ -1087,7 +1106,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
             const int row = krow(kbase + 16 * a + 4 * kq + i);
             const int cb = (16 * dt + lr) * 4;
             const float av = *reinterpret_cast<const float*>(
-                vb + row * ROWB + (((cb >> 4) ^ (row & SWZ)) << 4) + (cb & 15));
+                vb + row * ROWB + (((cb >> 4) ^ swz_key<T, D>(row)) << 4) + (cb & 15));
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pr[a][i], oacc[dt], 0, 0, 0);
           }
     }
