@@ -508,36 +508,27 @@ __device__ __forceinline__ void dma_offsets(uint32_t* off) {
   }
 }
 
-// lane's 16 bytes from [tile, tile + bytes) at byte offset voff, through a raw
-// buffer descriptor (tile wave-uniform, in scalar registers; the only vector
-// operand is the 32-bit offset; an offset past `bytes` reads zeros)
-__device__ __forceinline__ void lds_dma16_tile(const void* tile, uint32_t bytes, uint32_t voff,
-                                               void* lds_base) {
+// DMA one 64-token K or V tile (64 x D, row-major, swizzled) into LDS; every
+// wave moves KI kilobytes of it, to LDS addresses m0, m0 + 1024, ... (m0
+// wave-uniform, already offset for this wave).  `g` is wave-uniform.  The
+// per-lane offsets stay in the same registers for the whole item, so no
+// instruction writes a register that a transfer still in flight names (the
+// compiler would make it wait for every outstanding transfer first).
+template <typename T, int D>
+__device__ __forceinline__ void dma_block(const unsigned char* g, uint32_t m0, const uint32_t* off) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  using Gm = Geo<T, D>;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const uint64_t a = reinterpret_cast<uint64_t>(tile);
+  const uint64_t a = reinterpret_cast<uint64_t>(g);
   const u32x4 desc = {uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a))),
                       uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu)),
-                      uint32_t(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
-  const uint32_t m0 = uint32_t(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
-               "s"(desc)
-               : "memory");
-#endif
-}
-
-// DMA one 64-token K or V tile (64 x D, row-major, swizzled) into LDS; every
-// wave moves KI kilobytes of it.  `g` is wave-uniform.  The per-lane offsets
-// stay in the same registers for the whole item, so no instruction writes a
-// register that a transfer still in flight names (the compiler would make it
-// wait for every outstanding transfer first).
-template <typename T, int D>
-__device__ __forceinline__ void dma_block(const unsigned char* g, unsigned char* lds,
-                                          const uint32_t* off) {
-  using Gm = Geo<T, D>;
-  const int w = threadIdx.x >> 6;
+                      uint32_t(Gm::BLKB), 0x00020000u};
 #pragma unroll
-  for (int i = 0; i < Gm::KI; ++i) lds_dma16_tile(g, Gm::BLKB, off[i], lds + (w * Gm::KI + i) * 1024);
+  for (int i = 0; i < Gm::KI; ++i)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0 + 1024u * i),
+                 "v"(off[i]), "s"(desc)
+                 : "memory");
+#endif
 }
 
 // A 32-bit global load hidden from the compiler, landing in LDS (lane i's
@@ -839,13 +830,22 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   dma_offsets<T, D>(doff);
   const uint64_t bad = __ballot(lane < nblk && !(my_id >= 0 && my_id < p.num_blocks));
   if (bad != 0 && tid == 0) set_error(p.hdr, kErrBadPrefix);
-  auto issue = [&](int j) {
-    int id = __builtin_amdgcn_readfirstlane(__shfl(my_id, j));  // wave-uniform
+  // Block j goes to ring slot sl (= j % NS, which the callers keep as a
+  // counter).  Every address here is wave-uniform and in scalar registers: the
+  // block id comes by readlane, and the LDS side is this wave's part of the
+  // slot as a 32-bit LDS address.
+  const uint32_t ring_m0 =
+      uint32_t(__builtin_amdgcn_readfirstlane(lds_addr(ring))) +
+      uint32_t(__builtin_amdgcn_readfirstlane(w)) * uint32_t(KI * 1024);
+  const size_t blk_stride = size_t(p.hkv) * head_stride;  // elements per pool block
+  const size_t head_off = size_t(it.g) * head_stride;
+  auto issue = [&](int j, int sl) {
+    int id = __builtin_amdgcn_readlane(my_id, j);  // wave-uniform
     if ((bad >> j) & 1) id = 0;
-    unsigned char* slot = ring + (j % NS) * SLOTB;
-    const size_t base = (size_t(id) * p.hkv + it.g) * head_stride;
-    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), slot, doff);
-    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), slot + BLKB, doff);
+    const uint32_t m0 = ring_m0 + uint32_t(sl) * uint32_t(SLOTB);
+    const size_t base = size_t(uint32_t(id)) * blk_stride + head_off;
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_cache) + base), m0, doff);
+    dma_block<T, D>(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_cache) + base), m0 + BLKB, doff);
   };
   // tree segments (64 nodes each) go through the ring like KV blocks, after
   // the item's KV blocks (ring unit nblk + segment): in the split path's
@@ -855,9 +855,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // and tensor, like a KV block.
   const int nseg = (SUFFIX || (with_tree && big)) ? cdiv(si.T, kBlock) : 0;
   const int ntot = nblk + nseg;  // ring units of the item
-  auto stage = [&](int j) {
+  auto stage = [&](int j, int sl) {
     const int sg = j - nblk;
-    unsigned char* sk = ring + (j % NS) * SLOTB;
+    unsigned char* sk = ring + sl * SLOTB;
     for (int m = w; m < BLKB / 1024; m += kAttnWaves) {
       const int u = m * 64 + lane;
       const int t = min(kBlock * sg + u / KCH, si.T - 1);
@@ -870,11 +870,11 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
                 sk + BLKB + m * 1024);
     }
   };
-  auto issue_any = [&](int j) {
-    if (j < nblk) issue(j);
-    else stage(j);
+  auto issue_any = [&](int j, int sl) {
+    if (j < nblk) issue(j, sl);
+    else stage(j, sl);
   };
-  for (int j = 0; j < NS && j < ntot; ++j) issue_any(j);
+  for (int j = 0; j < NS && j < ntot; ++j) issue_any(j, j);
 
   // ---- tree staging: wait for the tree DMA (older than the blocks), then the
   // tree mask by pointer jumping (as in tree_mask_wave)
@@ -1117,8 +1117,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // for the whole loop, so the running output stays in place in registers.
   auto stream = [&](auto ks_tag, auto mask_tag, auto act_tag, int j0, int j1) {
     constexpr bool kMasked = decltype(mask_tag)::value;
+    int sl = j0 % NS;  // ring slot of block j
     for (int j = j0; j < j1; ++j) {
-      unsigned char* slot = ring + (j % NS) * SLOTB;
+      unsigned char* slot = ring + sl * SLOTB;
       wait_blocks<KI, NSMAX>(min(NS - 1, ntot - 1 - j));
       raw_barrier();
       int nv = kBlock;
@@ -1132,7 +1133,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       if constexpr (decltype(act_tag)::value)
         compute(std::false_type{}, ks_tag, mask_tag, slot, slot + BLKB, nv, 0);
       raw_barrier();
-      if (j + NS < ntot) issue_any(j + NS);
+      if (j + NS < ntot) issue_any(j + NS, sl);  // into the slot just freed
+      sl = sl + 1 == NS ? 0 : sl + 1;
     }
   };
   // the tree piece (while the first KV blocks are still in flight), then the
@@ -1142,8 +1144,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // each under its mask word from LDS
   auto big_segments = [&](auto ks_tag, auto act_tag) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(tree_lds);
+    int sl = nblk % NS;
     for (int j = nblk; j < ntot; ++j) {
-      unsigned char* slot = ring + (j % NS) * SLOTB;
+      unsigned char* slot = ring + sl * SLOTB;
       wait_blocks<KI, NSMAX>(min(NS - 1, ntot - 1 - j));
       raw_barrier();
       const int r = 16 * rt + lr;
@@ -1151,7 +1154,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       if constexpr (decltype(act_tag)::value)
         compute(std::true_type{}, ks_tag, std::true_type{}, slot, slot + BLKB, 0, word);
       raw_barrier();
-      if (j + NS < ntot) issue_any(j + NS);
+      if (j + NS < ntot) issue_any(j + NS, sl);
+      sl = sl + 1 == NS ? 0 : sl + 1;
     }
   };
   auto tree_and_stream = [&](auto ks_tag, auto act_tag) {
@@ -1171,16 +1175,18 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   };
   auto segments = [&](auto ks_tag, auto act_tag) {
     // unrolled, so that segw is indexed by constants and stays in registers
+    int sl = 0;
 #pragma unroll
     for (int sg = 0; sg < kSegMax; ++sg) {
       if (sg >= nseg) break;
-      unsigned char* slot = ring + (sg % NS) * SLOTB;
+      unsigned char* slot = ring + sl * SLOTB;
       wait_blocks<KI, NSMAX>(min(NS - 1, nseg - 1 - sg));
       raw_barrier();
       if constexpr (decltype(act_tag)::value)
         compute(std::true_type{}, ks_tag, std::true_type{}, slot, slot + BLKB, 0, segw[sg]);
       raw_barrier();
-      if (sg + NS < nseg) issue_any(sg + NS);
+      if (sg + NS < nseg) issue_any(sg + NS, sl);
+      sl = sl + 1 == NS ? 0 : sl + 1;
     }
   };
   if constexpr (SUFFIX) {
