@@ -194,7 +194,8 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
  * block table, so the tree K/V need no separate write.  Each table row must
  * cover P + T positions; a region block id outside [0, num_blocks) or a row
  * too short raises TA_ERR_BAD_PREFIX.  Same shape, workspace and outputs as
- * tree_attn_verify.  [pith.science verdict record: desk editor letter (paged
+ * tree_attn_verify, for trees of up to 64 nodes (max_tree_nodes <= 64, else
+ * TA_ERR_UNSUPPORTED).  [pith.science verdict record: desk editor letter (paged
  * KV with tree padding) and referee summary (paged/persistent KV-cache
  * handling for tree attention)] */
 ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const void* k_cache,
