@@ -298,7 +298,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         return 2
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
         print("bench.py is single-process; WORLD_SIZE > 1 is not supported", file=sys.stderr)
