@@ -1356,10 +1356,14 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // log-sum-exp weights.
   // [merge_attentions over disjoint KV chunks: pith.science verdict record,
   // pith_extraction.supporting_citations (Juravsky et al. 2024)]
-  {
+  // QMAX: partial loads per lane.  The solo combine of a group with many
+  // chunks takes four times as many, so that several rows go in each pass
+  // (each pass is one device-coherent round trip).
+  constexpr int kQBase = kMaxSplits / (kAttnThreads / (D / 4));
+  auto combine = [&](auto qmax_tag) {
     constexpr int L4 = D / 4;
     constexpr int NSLOT = kAttnThreads / L4;
-    constexpr int QMAX = kMaxSplits / NSLOT;
+    constexpr int QMAX = decltype(qmax_tag)::value;
     static_assert((NSLOT & (NSLOT - 1)) == 0, "row slots are a power of two");
     // QG row slots per row: enough that QMAX loads per lane cover the S
     // partials, and no more than lets all of this workgroup's rows go in one
@@ -1476,7 +1480,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       }
       __syncthreads();
     }
-  }
+  };
+  if (solo_combine && S > kQBase) combine(std::integral_constant<int, 4 * kQBase>{});
+  else combine(std::integral_constant<int, kQBase>{});
 }
 
 template <typename T, int D, bool FUSED, bool BIG = false>
