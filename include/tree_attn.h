@@ -25,7 +25,7 @@
  *   - Every pointer argument except `shape` is a DEVICE pointer owned by the
  *     caller.  The library never allocates or frees device memory and never
  *     synchronises, except tree_attn_get_error (documented below).  All calls
- *     are asynchronous on `stream` and safe to capture in a HIP graph.
+ *     are asynchronous on `stream`.
  *   - All tensors are dense, row-major, contiguous, at least 16-byte aligned.
  *   - Element type of q, k_cache, v_cache, k_tree, v_tree and `out` is
  *     shape->dtype (bf16 = raw 16-bit patterns, or fp32).  Partial outputs
@@ -60,7 +60,15 @@
  *     tree_attn_get_error reports.  Outputs of an affected sequence are then
  *     unspecified.
  *   - Thread safety: calls may come from any host thread.  Calls that run
- *     concurrently (different streams) must use different workspaces.
+ *     concurrently (different streams) must use different workspaces.  A
+ *     call never needs the whole GPU to itself: the work items of one
+ *     launch that meet to combine their partial results wait only for items
+ *     that are already running, so concurrent calls, or other kernels
+ *     holding some of the CUs, delay a call but cannot stall it.
+ *   - Graph capture: after a first call of a shape outside any capture (it
+ *     sets a kernel attribute once), every call issues only kernel launches,
+ *     so a sequence of calls can be captured into a HIP graph and replayed
+ *     with new data in the same buffers.
  */
 #ifndef TREE_ATTN_H_
 #define TREE_ATTN_H_
@@ -290,6 +298,23 @@ const char* tree_attn_status_string(ta_status status);
 /* Work-item size (prefix tokens per work item) the library would use for
  * `shape`; 0 if the shape is invalid.  For inspection and benchmarking. */
 int32_t tree_attn_split_tokens(const ta_shape* shape);
+
+/* How tree_attn_verify would launch for `shape` (host values only; no device
+ * call beyond cached device attributes).  info (host int32 [4]) receives:
+ *   info[0]  prefix tokens per work item (a multiple of 64; the kernel may
+ *            pick a smaller one from the actual prefix lengths when info[3]
+ *            is 2 and split_tokens is 0)
+ *   info[1]  workgroups of the launch (one per CU at most)
+ *   info[2]  bound on the work items (workspace partial slots)
+ *   info[3]  0: every item runs in the first round and the chunks of a group
+ *               split the final combine (they meet at a barrier, waiting only
+ *               for chunks that have started);
+ *            1: more items than workgroups: items are handed out by ticket
+ *               and the last chunk of each group to arrive combines it alone;
+ *            2: decided on the device from the actual prefix lengths (0 when
+ *               the items fit the first round, else 1).
+ * TA_ERR_INVALID_ARG for a null info; shape errors as tree_attn_verify. */
+ta_status tree_attn_launch_info(const ta_shape* shape, int32_t* info);
 
 #ifdef __cplusplus
 }

@@ -136,3 +136,27 @@ def test_large_trees_verify_and_split_only(T):
     assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), None, 1 << 40, None) == 4
     assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), FAKE, 1 << 40, None) == 2
     assert lib.tree_attn_accept_greedy(ctypes.byref(s), *([FAKE] * 7), FAKE, 1 << 40, None) == 2
+
+
+def test_launch_info_mode_choice():
+    """The host's launch plan (no GPU here: sized for a full MI355X, one
+    workgroup per CU on 256 CUs)."""
+    # one sequence, 8 KV heads, 8192 tokens: every item in the first round
+    i = ta.launch_info(shape())
+    assert i["mode"] == "first_round"
+    assert i["max_items"] == 8 * -(-8192 // i["split_tokens"]) and i["max_items"] <= i["grid"] <= 256
+    # one sequence forced into small chunks: at most 64 chunks a group (64 tokens
+    # become 128), 8 * 64 items handed out by ticket
+    i = ta.launch_info(shape(split_tokens=64))
+    assert i["split_tokens"] == 128
+    assert i["mode"] == "ticket" and i["max_items"] == 512 and i["grid"] == 256
+    # more groups than workgroups: ticket mode whatever the prefix lengths
+    i = ta.launch_info(shape(batch=256, max_prefix_len=32768, max_blocks_per_seq=512,
+                             total_tree_nodes=1536))
+    assert i["mode"] == "ticket"
+    # a batch whose groups fit the grid: the kernel picks the chunk from the actual lengths
+    i = ta.launch_info(shape(batch=32, num_q_heads=8, num_kv_heads=1, total_tree_nodes=128))
+    assert i["mode"] == "device"
+    with pytest.raises(ta.TreeAttnError):
+        ta.launch_info(shape(head_dim=96))
+    assert load().tree_attn_launch_info(ctypes.byref(shape()), None) == 1

@@ -135,26 +135,56 @@ def test_verify_configs(idx):
     _check_verify(inp, out, lse, f"cfg{idx}")
 
 
-def test_verify_cfg5_full_size_sampled():
+def test_verify_cfg5_full_size():
+    """The ragged batch-256 workload at full size, in the benchmark's launch
+    configuration (library chunking, items handed out by ticket, the last
+    chunk of a group combining alone): every row and head against the oracle."""
+    import tree_attention_verify_attn_amd as ta
     inp = make_config(5)
     d = to_device(inp)
-    say("verify cfg5 full size")
+    say(f"verify cfg5 full size, split_tokens {ta.split_tokens(d.shape)}")
     out, lse = run_verify(d)
-    import tree_attention_verify_attn_amd as ta
     assert ta.get_error(d.workspace) == 0
-    o, l = host(out), host(lse)
-    assert np.isfinite(o).all() and np.isfinite(l).all()
-    rng = np.random.default_rng(5)
-    N, Hq = inp.total_tree_nodes, inp.num_q_heads
-    # longest, shortest and random rows
-    seq_of = np.searchsorted(inp.tree_offsets, np.arange(N), side="right") - 1
-    P = inp.prefix_lens[seq_of]
-    picks = [int(np.argmax(P)), int(np.argmin(P)), N - 1, 0] + list(rng.integers(0, N, 60))
-    rows = [(n, int(rng.integers(0, Hq))) for n in picks]
-    wo, wl = oracle.verify_rows(inp, rows)
-    for k, (n, h) in enumerate(rows):
-        assert np.max(np.abs(o[n, h] - wo[k])) <= 2e-2, (n, h)
-        assert abs(l[n, h] - wl[k]) <= 1e-3, (n, h)
+    _check_verify(inp, out, lse, "cfg5 full size")
+
+
+def _ticket_inputs(seed, *, B, lens, D=128, Hq=8, Hkv=2, trees=None):
+    return small_inputs(seed, dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, D=D,
+                        prefix_lens=tuple(int(x) for x in lens),
+                        trees=trees or [TREE_12] * B)
+
+
+# Many groups of many chunks: more items than workgroups, so items are handed
+# out by ticket and the chunk that arrives last combines its group alone; with
+# more than 4 chunks per group (2 at D = 64) that combine loads several chunk
+# partials per lane and folds several rows per pass.
+TICKET_CASES = [
+    # 64-token chunks, 5..64 chunks per group
+    ("split64-d128", lambda: _ticket_inputs(
+        400, B=40, lens=np.random.default_rng(400).integers(321, 4097, 40)), 64),
+    ("split64-d64", lambda: _ticket_inputs(
+        401, B=40, D=64, lens=np.random.default_rng(401).integers(321, 4097, 40)), 64),
+    # 300 sequences of mixed length, 1024-token chunks (1..6 chunks per group)
+    ("300seq-split1024", lambda: _ticket_inputs(
+        402, B=300, Hq=8, Hkv=1, trees=[[-1, 0, 1, 2]] * 300,
+        lens=np.random.default_rng(402).integers(16, 6001, 300)), 1024),
+]
+
+
+@pytest.mark.parametrize("name,make,split", TICKET_CASES, ids=[c[0] for c in TICKET_CASES])
+def test_verify_ticket_many_chunks(name, make, split):
+    import tree_attention_verify_attn_amd as ta
+    inp = make()
+    d = to_device(inp, split_tokens=split)
+    S = [max(1, -(-int(p) // split)) for p in inp.prefix_lens]
+    say(f"verify ticket mode {name}: {sum(S) * inp.num_kv_heads} items, "
+        f"chunks per group {min(S)}..{max(S)}")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, f"ticket {name}")
+    # the same call again on the same workspace: the counters reset themselves
+    out2, lse2 = run_verify(d)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
 @pytest.mark.parametrize("split", [64, 128, 256, 1024, 4096])

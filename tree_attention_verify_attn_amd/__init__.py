@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     merge,
     prefix,
     split_tokens,
+    launch_info,
     status_string,
     suffix,
     verify,

@@ -49,6 +49,7 @@ EXPORTED = (
     "tree_attn_get_error",
     "tree_attn_status_string",
     "tree_attn_split_tokens",
+    "tree_attn_launch_info",
 )
 
 _lib = None
@@ -70,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "tree_attn_workspace_size": (S, [SP]),
         "tree_attn_split_tokens": (I32, [SP]),
+        "tree_attn_launch_info": (I32, [SP, P]),
         "tree_attn_workspace_init": (I32, [P, S, P]),
         "tree_attn_build_mask": (I32, [SP, P, P, P, P, S, P]),
         "tree_attn_prefix": (I32, [SP, P, P, P, P, P, P, P, P, P, S, P]),

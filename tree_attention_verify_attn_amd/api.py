@@ -81,6 +81,14 @@ def split_tokens(shape: Shape) -> int:
     return int(load().tree_attn_split_tokens(ctypes.byref(shape)))
 
 
+def launch_info(shape: Shape) -> dict:
+    """How tree_attn_verify would launch for `shape` (tree_attn_launch_info)."""
+    info = (ctypes.c_int32 * 4)()
+    _check(load().tree_attn_launch_info(ctypes.byref(shape), info), "tree_attn_launch_info")
+    return {"split_tokens": info[0], "grid": info[1], "max_items": info[2],
+            "mode": ("first_round", "ticket", "device")[info[3]]}
+
+
 def alloc_workspace(shape: Shape, device="cuda", min_bytes: int = 256) -> torch.Tensor:
     """Zero-filled workspace (torch allocation; the library itself never allocates)."""
     n = max(workspace_size(shape), min_bytes)

@@ -2,6 +2,7 @@
 // size heuristic, and kernel launches.  The C entry points are declared and
 // documented in include/tree_attn.h.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -51,6 +52,36 @@ int occupancy(const void* kernel, size_t dyn) {
   if (occ < 0) occ = 0;
   cache[key] = occ;
   return occ;
+}
+
+// Raise a kernel's dynamic-LDS limit to at least `dyn` bytes.  The attribute
+// is set once per kernel, device and size, not on every call, so that calls
+// made while a stream is being captured into a graph make no runtime call
+// beyond the launch itself (the first call of a shape, usually made outside
+// any capture, sets it).
+int ensure_dyn_lds(const void* kernel, size_t dyn) {
+  static std::mutex mu;
+  static std::unordered_map<unsigned long long, size_t> done;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const unsigned long long key =
+      reinterpret_cast<unsigned long long>(kernel) ^ (static_cast<unsigned long long>(dev) << 48);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = done.find(key);
+  if (it != done.end() && it->second >= dyn) return kOk;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn)) != hipSuccess)
+    return kErrHip;
+  done[key] = dyn;
+  return kOk;
+}
+
+// Test hook, read on every call: with TREE_ATTN_TEST_FORCE_LEAVE=1 in the
+// environment, the odd chunks of every first-round group leave the meeting
+// without waiting, as they do when the rest of their group has not started
+// (the results must not change).  Never needed outside the tests.
+int test_force_leave() {
+  const char* v = getenv("TREE_ATTN_TEST_FORCE_LEAVE");
+  return v && v[0] == '1' ? 1 : 0;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -238,6 +269,7 @@ Params base_params(const ta_shape* s, const WsLayout& L, void* ws) {
   p.single_items = p.single ? s->num_kv_heads * cdiv(s->total_tree_nodes * p.group, kRowsPerPass) * L.s_max : 0;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf(float(s->head_dim));
   p.scale_log2 = scale * kLog2e;
+  p.force_leave = test_force_leave();
   char* w = static_cast<char*>(ws);
   p.hdr = reinterpret_cast<WsHeader*>(w);
   if (w) {
@@ -287,8 +319,7 @@ int launch_suffix(const ta_shape* s, Params p, unsigned grid, hipStream_t stream
   p.ns = ns;
   p.tree_lds_half = 0;
   const size_t dyn = size_t(ns) * slot;
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn)) != hipSuccess)
-    return kErrHip;
+  if (ensure_dyn_lds(kern, dyn) != kOk) return kErrHip;
   hipLaunchKernelGGL((suffix_kernel<T, D>), dim3(grid), dim3(kAttnThreads), dyn, stream, p);
   return launch_status();
 }
@@ -301,8 +332,7 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
   p.ns = ring_slots(s, FUSED);
   if (p.ns < 1) return kErrUnsupported;  // tree rows + sequence table leave no room for the ring
   const size_t dyn = attn_dyn_lds(s, FUSED);
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn)) != hipSuccess)
-    return kErrHip;
+  if (ensure_dyn_lds(kern, dyn) != kOk) return kErrHip;
   const int cus = device_info().cus;
   if (cus <= 0) return kErrHip;
   const int occ = occupancy(kern, dyn);
@@ -349,6 +379,39 @@ int check_ws(const ta_shape* s, const WsLayout& L, void* ws, size_t ws_bytes) {
   return kOk;
 }
 
+// tree_attn_verify on a given workspace (argument checks, layout, launch).
+int fused_verify(const ta_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, const int32_t* prefix_lens, const void* k_tree,
+                 const void* v_tree, const int32_t* parents, const int32_t* tree_offsets,
+                 void* out, float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != kOk) return st;
+  if (!prefix_lens || !tree_offsets || !block_table) return kErrInvalidArg;
+  if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !parents || !out))
+    return kErrInvalidArg;
+  if (shape->max_prefix_len > 0 && (!k_cache || !v_cache)) return kErrInvalidArg;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
+      !aligned16(v_tree))
+    return kErrInvalidArg;
+  WsLayout L = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true));
+  st = check_ws(shape, L, ws, ws_bytes);
+  if (st != kOk) return st;
+  if (shape->total_tree_nodes == 0) return kOk;
+  Params p = base_params(shape, L, ws);
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.prefix_lens = prefix_lens;
+  p.k_tree = k_tree;
+  p.v_tree = v_tree;
+  p.parents = parents;
+  p.tree_offsets = tree_offsets;
+  p.out = out;
+  p.lse_out = lse_out;
+  return dispatch_attn<true>(shape, p, L, stream);
+}
+
 }  // namespace
 }  // namespace ta
 
@@ -366,6 +429,29 @@ size_t tree_attn_workspace_size(const ta_shape* shape) {
 int32_t tree_attn_split_tokens(const ta_shape* shape) {
   if (check_shape(shape) != kOk) return 0;
   return choose_chunk(shape, true);
+}
+
+ta_status tree_attn_launch_info(const ta_shape* shape, int32_t* info) {
+  if (!info) return TA_ERR_INVALID_ARG;
+  const int st = check_shape(shape);
+  if (st != kOk) return static_cast<ta_status>(st);
+  const int chunk = choose_chunk(shape, true);
+  const WsLayout L = layout_for(shape, chunk, auto_cap(shape, true));
+  const int cap = grid_capacity(shape, true);
+  int grid = L.item_slots < cap ? L.item_slots : cap;
+  if (grid < 1) grid = 1;
+  int mode;
+  if (one_sequence(shape))
+    mode = L.item_slots <= grid ? 0 : 1;  // items numbered statically: the count is known here
+  else if (chunk_auto(shape))
+    mode = L.num_groups > grid ? 1 : 2;   // the kernel fits every item in the first round if it can
+  else
+    mode = L.item_slots <= grid ? 0 : 2;  // a fixed chunk: the actual prefix lengths decide
+  info[0] = chunk;
+  info[1] = grid;
+  info[2] = L.item_slots;
+  info[3] = mode;
+  return TA_OK;
 }
 
 ta_status tree_attn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -487,32 +573,9 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
                            const int32_t* prefix_lens, const void* k_tree, const void* v_tree,
                            const int32_t* parents, const int32_t* tree_offsets, void* out,
                            float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_shape(shape);
-  if (st != kOk) return static_cast<ta_status>(st);
-  if (!prefix_lens || !tree_offsets || !block_table) return TA_ERR_INVALID_ARG;
-  if (shape->total_tree_nodes > 0 && (!q || !k_tree || !v_tree || !parents || !out))
-    return TA_ERR_INVALID_ARG;
-  if (shape->max_prefix_len > 0 && (!k_cache || !v_cache)) return TA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
-      !aligned16(v_tree))
-    return TA_ERR_INVALID_ARG;
-  WsLayout L = layout_for(shape, choose_chunk(shape, true), auto_cap(shape, true));
-  st = check_ws(shape, L, ws, ws_bytes);
-  if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->total_tree_nodes == 0) return TA_OK;
-  Params p = base_params(shape, L, ws);
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_table = block_table;
-  p.prefix_lens = prefix_lens;
-  p.k_tree = k_tree;
-  p.v_tree = v_tree;
-  p.parents = parents;
-  p.tree_offsets = tree_offsets;
-  p.out = out;
-  p.lse_out = lse_out;
-  return static_cast<ta_status>(dispatch_attn<true>(shape, p, L, stream));
+  return static_cast<ta_status>(fused_verify(shape, q, k_cache, v_cache, block_table, prefix_lens,
+                                             k_tree, v_tree, parents, tree_offsets, out, lse_out,
+                                             ws, ws_bytes, stream));
 }
 
 ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const void* k_cache,

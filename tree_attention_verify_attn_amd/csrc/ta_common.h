@@ -36,6 +36,10 @@ enum : int {
 };
 
 constexpr int kCounterStride = 64;  // unsigned words between two counters: one 256-byte line each
+// words of a group's line in the barrier region: arrival counter at 0, then
+constexpr int kStartedWord = 8;     // chunks of the group that have started
+constexpr int kLeaveWord = 16;      // 64-bit mask of chunks that left without waiting
+constexpr int kSenseWord = 32;      // sense word the waiting chunks poll
 constexpr int kBarrierSlots = 1024; // group barriers in the workspace's fixed region (grid size bound)
 constexpr int kMaxGroups = 1 << 18; // ticket arrival counters: batch * kv heads * row passes, at most
 
@@ -96,6 +100,7 @@ struct Params {
   int first_round;           // workgroups in the grid
   int tree_lds_half;         // LDS bytes for tree K (and again for tree V); multiple of 1 KiB
   int ns;                    // KV ring slots in LDS, 1..kMaxRingSlots
+  int force_leave;           // test hook: odd chunks of first-round groups leave without waiting
   float scale_log2;          // softmax_scale * log2(e)
 };
 

@@ -415,7 +415,8 @@ constexpr int kHidSense = 0;                  // the group's sense word (thread 
 constexpr int kHidOff = 1;                    // tree_offsets[0], [1] (wave 0, lanes 0 and 1)
 constexpr int kHidP = 4;                      // the prefix length, per wave
 constexpr int kHidBlk = kHidP + kAttnWaves;   // two tree-region block ids, per wave
-constexpr int kHidWords = kHidBlk + 2 * kAttnWaves;
+constexpr int kHidStarted = kHidBlk + 2 * kAttnWaves;  // the group's started count (thread 0)
+constexpr int kHidWords = kHidStarted + 1;
 
 struct SmemMisc {
   uint64_t mask[kMaxTree];
@@ -673,7 +674,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // clamped index and goes unused).
   const int first_item = slot_index - it.s;
   unsigned* const bar = p.arrive + size_t(min(first_item, kBarrierSlots - 1)) * kCounterStride;
-  unsigned* const sense = bar + kCounterStride / 2;
+  unsigned* const sense = bar + kSenseWord;
+  unsigned* const started = bar + kStartedWord;
+  unsigned long long* const leaving = reinterpret_cast<unsigned long long*>(bar + kLeaveWord);
   unsigned* const counter =
       solo_combine ? p.arrive + size_t(kBarrierSlots) * kCounterStride + size_t(it.grp) : bar;
   // nothing of the previous item is still in flight (free for the first item):
@@ -761,6 +764,12 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   const int nblk = cdiv(ntok, kBlock);
   const int S = si.S;
   const bool with_tree = FUSED && it.s == S - 1;  // the last chunk also attends to the tree
+  // The chunks of a first-round group of several chunks meet after their
+  // partials are written.  Each counts itself as started here, once its
+  // chunk is known to be non-empty and before its first KV transfer, so
+  // that the meeting can tell whether every chunk of the group is running.
+  const bool meet = !SUFFIX && !solo_combine && S > 1;
+  if (meet && tid == 0) __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // trees of more than 64 nodes (fused): their 64-node segments follow the
   // chunk's KV blocks through the ring, under mask words built in LDS
   constexpr bool big = FUSED && BIG;
@@ -1279,6 +1288,10 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     unsigned char* stage = ring;    // free once the key parts are merged
     float* slotp = p.partials + size_t(slot_index) * p.slot_floats;
     const uint32_t sbytes = uint32_t(p.slot_floats) * 4u;
+    // the group's started count, read while the partial is being stored
+    // (hidden, like the sense word: it lands in LDS and is read after the
+    // wait below)
+    if (meet && tid == 0) hidden_load<true>(reinterpret_cast<const int*>(started), &sm.hid[kHidStarted]);
     __syncthreads();
     if (kp == 0 && active) {
       const int r = 16 * rt + lr;
@@ -1308,12 +1321,21 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   //   solo_combine (items are handed out over several rounds, so the chunks
   //   of a group may run far apart in time): nobody waits; the chunk that
   //   arrives last combines every row of the group.
-  //   otherwise (all chunks run at once): a sense-reversing barrier -- the
-  //   last arrival flips the group's sense word, the others poll it -- and
-  //   the S chunks then split the rows of the combine.
+  //   otherwise (all chunks normally run at once): the S chunks split the
+  //   rows of the combine, chunk s taking rows s, s + S, ...  A chunk waits
+  //   for the others only when the started count it read shows every chunk
+  //   of the group running: a running chunk always arrives, so that wait
+  //   ends even when the launch does not hold the whole GPU (another kernel,
+  //   or another verify call on another stream, may hold some of the CUs).
+  //   Otherwise it records itself in the group's leaving mask before it
+  //   arrives, and leaves.  The last arrival resets the counters, flips the
+  //   group's sense word, which the waiting chunks poll (a sense-reversing
+  //   barrier), and combines its own rows and those of every chunk that
+  //   left, exactly as that chunk would have.
   wait_all_mem();  // this wave's partial stores are complete
   __syncthreads();
-  int r0 = it.s, rstride = S;  // rows this workgroup combines: r0, r0 + rstride, ...
+  uint64_t rows_of = uint64_t(1) << (it.s & 63);  // chunks whose rows this workgroup combines
+  bool combine_all = false;
   if (solo_combine) {
     if (tid == 0) {
       const bool last = atomicAdd(counter, 1u) == unsigned(S - 1);
@@ -1322,29 +1344,45 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     }
     __syncthreads();
     if (!sm.bcast[2]) return;
-    r0 = 0;
-    rstride = 1;
+    combine_all = true;
   } else {
     if (tid == 0) {
-      unsigned spins = 0;
-      int timed_out = 0;
+      const unsigned st = unsigned(sm.hid[kHidStarted]);
+      const bool leave = st < unsigned(S) || (p.force_leave && (it.s & 1));
+      if (leave) {
+        // complete before the arrival that publishes it
+        __hip_atomic_fetch_or(leaving, 1ull << it.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_all_mem();
+      }
+      unsigned long long extra = 0;
+      int outcome = 0;  // 0: combine, 1: leave, 2: timed out
       if (atomicAdd(counter, 1u) == unsigned(S - 1)) {
+        // every chunk has arrived, and every leaver's bit was set before its arrival
+        extra = __hip_atomic_load(leaving, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(started, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (extra) __hip_atomic_store(leaving, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(sense, sense0 ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (leave) {
+        outcome = 1;
       } else {
+        unsigned spins = 0;
         while (ld_counter(sense) == sense0) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kSpinLimit) {
-            timed_out = 1;
+            outcome = 2;
             break;
           }
         }
+        if (outcome == 2) set_error(p.hdr, kErrTimeout);
       }
-      if (timed_out) set_error(p.hdr, kErrTimeout);
-      sm.bcast[2] = timed_out;
+      sm.bcast[2] = outcome;
+      sm.bcast[0] = int(uint32_t(extra));
+      sm.bcast[1] = int(uint32_t(extra >> 32));
     }
     __syncthreads();
     if (sm.bcast[2]) return;
+    rows_of |= (uint64_t(uint32_t(sm.bcast[1])) << 32) | uint32_t(sm.bcast[0]);
   }
 
   // ---- combine.  This workgroup takes rows r0, r0 + rstride, ... of the
@@ -1360,7 +1398,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // chunks takes four times as many, so that several rows go in each pass
   // (each pass is one device-coherent round trip).
   constexpr int kQBase = kMaxSplits / (kAttnThreads / (D / 4));
-  auto combine = [&](auto qmax_tag) {
+  auto combine = [&](auto qmax_tag, int r0, int rstride) {
     constexpr int L4 = D / 4;
     constexpr int NSLOT = kAttnThreads / L4;
     constexpr int QMAX = decltype(qmax_tag)::value;
@@ -1481,8 +1519,17 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       __syncthreads();
     }
   };
-  if (solo_combine && S > kQBase) combine(std::integral_constant<int, 4 * kQBase>{});
-  else combine(std::integral_constant<int, kQBase>{});
+  if (combine_all) {
+    if (S > kQBase) combine(std::integral_constant<int, 4 * kQBase>{}, 0, 1);
+    else combine(std::integral_constant<int, kQBase>{}, 0, 1);
+  } else {
+    // rows of chunk c: c, c + S, ... (this chunk's own, then any that left)
+    while (rows_of) {
+      const int c = __builtin_ctzll(rows_of);
+      rows_of &= rows_of - 1;
+      combine(std::integral_constant<int, kQBase>{}, c, S);
+    }
+  }
 }
 
 template <typename T, int D, bool FUSED, bool BIG = false>
