@@ -91,7 +91,9 @@ typedef enum {
   TA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
   TA_ERR_BAD_PREFIX = 6,   /* device-detected: prefix length or block id out of range */
   TA_ERR_TIMEOUT = 7,      /* device-detected: a bounded cross-workgroup wait gave up */
-  TA_ERR_NO_BLOCKS = 8     /* device-detected: free list or block-table row too small */
+  TA_ERR_NO_BLOCKS = 8,    /* device-detected: free list or block-table row too small */
+  TA_ERR_SCRATCH = 9       /* the shape needs more workspace than tree_attn_verify_noalloc's
+                              static scratch holds */
 } ta_status;
 
 typedef enum { TA_DTYPE_F32 = 0, TA_DTYPE_BF16 = 1 } ta_dtype;
@@ -286,6 +288,29 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
                            int32_t* prefix_lens, const int32_t* free_blocks, int32_t free_count,
                            int32_t* blocks_taken, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/* tree_attn_verify without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same inputs, outputs, semantics and
+ * kernels as tree_attn_verify; the workspace is instead a static device array
+ * of the library (32 MiB, one per GPU the library runs on, held until the
+ * process ends; its address is taken once per device on the first call there).
+ * The call allocates and frees nothing.  Shapes whose tree_attn_workspace_size
+ * exceeds 32 MiB return TA_ERR_SCRATCH before anything is launched (e.g. a
+ * batch of 256 long ragged sequences: use tree_attn_verify there).
+ * device_status (device int32, may be NULL) receives the call's device-side
+ * error code (TA_OK, TA_ERR_BAD_TREE, TA_ERR_BAD_PREFIX or TA_ERR_TIMEOUT)
+ * when the call's kernels have run; a second small kernel on the stream
+ * writes it, clears the flag and, after an error, clears the static array's
+ * counters.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (two streams, two host threads) race and must not be
+ * made; calls in order on one stream are fine. */
+ta_status tree_attn_verify_noalloc(const ta_shape* shape, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* prefix_lens, const void* k_tree,
+                                   const void* v_tree, const int32_t* parents,
+                                   const int32_t* tree_offsets, void* out, float* lse_out,
+                                   int32_t* device_status, hipStream_t stream);
 
 /* Synchronises `stream`, reads and clears the device error flag of workspace
  * `ws` and returns it (TA_OK if no kernel flagged anything).  This is the only

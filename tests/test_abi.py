@@ -109,7 +109,7 @@ def test_merge_argument_checks():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert ta.status_string(code) and ta.status_string(code) != "unknown status"
     assert ta.status_string(99) == "unknown status"
 

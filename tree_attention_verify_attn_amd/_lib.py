@@ -42,6 +42,7 @@ EXPORTED = (
     "tree_attn_suffix",
     "tree_attn_merge",
     "tree_attn_verify",
+    "tree_attn_verify_noalloc",
     "tree_attn_verify_incache",
     "tree_attn_commit_incache",
     "tree_attn_accept_greedy",
@@ -78,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tree_attn_suffix": (I32, [SP, P, P, P, P, P, P, P, P]),
         "tree_attn_merge": (I32, [I64, I32, I32, P, P, P, P, P, P, P]),
         "tree_attn_verify": (I32, [SP, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
+        "tree_attn_verify_noalloc": (I32, [SP, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "tree_attn_verify_incache": (I32, [SP, P, P, P, P, P, P, P, P, P, P, S, P]),
         "tree_attn_commit_incache": (I32, [SP, P, P, P, P, P, P, P, P, P, S, P]),
         "tree_attn_accept_greedy": (I32, [SP, P, P, P, P, P, P, P, P, S, P]),

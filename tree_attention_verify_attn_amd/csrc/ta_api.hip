@@ -754,8 +754,11 @@ const char* tree_attn_status_string(ta_status status) {
     case TA_ERR_BAD_PREFIX: return "prefix length or KV block id out of range (device check)";
     case TA_ERR_TIMEOUT: return "a bounded cross-workgroup wait gave up (device check)";
     case TA_ERR_NO_BLOCKS: return "free list or block-table row too small for the commit (device check)";
+    case TA_ERR_SCRATCH: return "shape needs more workspace than the no-allocation entry point's static scratch";
   }
   return "unknown status";
 }
 
 }  // extern "C"
+
+#include "ta_noalloc.hip"

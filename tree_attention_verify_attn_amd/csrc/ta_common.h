@@ -33,6 +33,7 @@ enum : int {
   kErrBadPrefix = 6,
   kErrTimeout = 7,
   kErrNoBlocks = 8,
+  kErrScratch = 9,
 };
 
 constexpr int kCounterStride = 64;  // unsigned words between two counters: one 256-byte line each
