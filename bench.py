@@ -118,8 +118,19 @@ def measured_traffic(config_index: int, split: int):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, budget_s: float, nbytes: int):
-    import numpy as np
+    import numpy as np  # noqa: F401
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -127,6 +138,7 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     calls = 0
+    c0 = time.process_time()
     t0 = time.perf_counter()
     while True:
         oracle.verify(inp)
@@ -134,6 +146,7 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    cpu_s = time.process_time() - c0
     per = el / calls
     return {
         "value": nbytes / per / 1e9,
@@ -141,9 +154,68 @@ def cpu_baseline(inp, budget_s: float, nbytes: int):
         "us_per_call": per * 1e6,
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{calls} full fp64 oracle verify call(s) of the benchmark workload "
-                  f"({el:.1f} s of CPU time)",
+        "sample": f"{calls} full fp64 oracle verify call(s) of the benchmark workload, "
+                  f"{el:.1f} s wall clock ({cpu_s:.1f} s of process CPU time) on {cpu_model()}, "
+                  f"{threads} BLAS threads",
+        "clock": "wall",
     }
+
+
+def summarize_trace(path: str, kernel: str) -> dict:
+    """Per-dispatch duration statistics of the kernels whose name contains
+    `kernel`, from a rocprofv3 --kernel-trace CSV (kernel_trace.csv)."""
+    import csv
+    import statistics
+    durs = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel in row.get("Kernel_Name", ""):
+                durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    if not durs:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel!r} in {path}")
+    q = statistics.quantiles(durs, n=10, method="inclusive")
+    return {"kernel": kernel, "dispatches": len(durs), "mean_us": round(statistics.fmean(durs), 3),
+            "p10_us": round(q[0], 3), "median_us": round(statistics.median(durs), 3),
+            "p90_us": round(q[8], 3), "min_us": round(min(durs), 3), "max_us": round(max(durs), 3)}
+
+
+def floor_run(torch, nbytes: int, steps: int, replica_bytes: float) -> dict:
+    """Reference floors for a launch that streams `nbytes` from HBM, timed like
+    the benchmark (rotating replicas of at least `replica_bytes` in total so
+    every step reads HBM, the GPU held while the host queues the K steps, one
+    event pair around them): a device-wide sum of the bytes (read only), a
+    device copy of them (read + write), and a one-workgroup empty launch."""
+    n = nbytes // 2
+    R = max(1, math.ceil(replica_bytes / nbytes))
+    src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    dst = [torch.empty_like(x) for x in src]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    torch.cuda._sleep(1_000_000)
+    s1.record()
+    torch.cuda.synchronize()
+    per_cycle_ms = max(s0.elapsed_time(s1), 1e-3) / 1_000_000
+
+    def timed(fn):
+        for i in range(10):
+            fn(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int((20.0 + 0.1 * steps) / per_cycle_ms))
+        e0.record()
+        for i in range(steps):
+            fn(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    read_us = timed(lambda r: torch.sum(src[r], dtype=torch.float32))
+    copy_us = timed(lambda r: dst[r].copy_(src[r]))
+    empty_us = timed(lambda r: torch.cuda._sleep(0))
+    return {"floor_bytes": 2 * n, "replicas": R, "steps": steps,
+            "sum_read_us": round(read_us, 3), "sum_read_GBps": round(2 * n / read_us / 1e3, 1),
+            "copy_us": round(copy_us, 3), "copy_GBps_read_plus_write": round(4 * n / copy_us / 1e3, 1),
+            "empty_launch_us": round(empty_us, 3)}
 
 
 def incache_layout(inp):
@@ -291,11 +363,22 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-after-verify", action="store_true",
                     help="skip timing greedy acceptance and the cache commit")
+    ap.add_argument("--floor", action="store_true",
+                    help="instead of the benchmark, time plain device reads and copies of the "
+                         "workload's algorithmic bytes (reference floors), one JSON line")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-dispatch p10 / median / p90 of the attention kernel from a "
+                         "rocprofv3 --kernel-trace CSV and exit (no GPU needed)")
+    ap.add_argument("--trace-kernel", default="attn_kernel",
+                    help="kernel-name substring for --summarize-trace")
     ap.add_argument("--copy-bytes", type=float, default=0.0,
                     help="instead of the benchmark, run --steps plain device-to-device copies "
                          "of this many bytes (reference for the HBM traffic counters)")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.trace_kernel)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -328,6 +411,11 @@ def main() -> int:
 
     log(f"building workload cfg{args.config}")
     inp = make_config(args.config)
+    if args.floor:
+        res = floor_run(torch, algorithmic_bytes(inp), args.steps, args.replica_bytes)
+        res["workload"] = CONFIG_NAMES[args.config]
+        print(json.dumps(res), flush=True)
+        return 0
     if inp.max_tree_nodes > 64 and args.entry == "incache":
         log("in-cache tree rows are for trees of up to 64 nodes; using the fused verify")
         args.entry = "verify"
