@@ -108,10 +108,9 @@ typedef struct {
   int32_t head_dim;           /* D in {64, 128} */
   int32_t block_size;         /* tokens per KV block; must be 64 */
   int32_t max_blocks_per_seq; /* row stride of block_table, >= 1 */
-  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size: 1..256 for the
-                                 fused verify and the split path (build_mask, prefix,
-                                 suffix, merge); 1..64 for the in-cache verify,
-                                 acceptance and commit */
+  int32_t max_tree_nodes;     /* upper bound on any sequence's tree size, 1..256 (up to
+                                 64 nodes a tree takes one 64-bit mask word per node,
+                                 beyond that ceil(T/64) words) */
   int32_t max_prefix_len;     /* upper bound on prefix_lens[b], 0..64*max_blocks_per_seq */
   int32_t total_tree_nodes;   /* N = tree_offsets[B] */
   int32_t num_blocks;         /* pool size: valid block ids are [0, num_blocks) */
@@ -202,10 +201,10 @@ ta_status tree_attn_verify(const ta_shape* shape, const void* q, const void* k_c
  * block block_table[b][(P+i)/64]).  The prefix piece covers positions
  * [0, P) as in tree_attn_verify; the tree piece reads its rows through the
  * block table, so the tree K/V need no separate write.  Each table row must
- * cover P + T positions; a region block id outside [0, num_blocks) or a row
- * too short raises TA_ERR_BAD_PREFIX.  Same shape, workspace and outputs as
- * tree_attn_verify, for trees of up to 64 nodes (max_tree_nodes <= 64, else
- * TA_ERR_UNSUPPORTED).  [pith.science verdict record: desk editor letter (paged
+ * cover P + T positions (a region of up to 5 blocks for 256 nodes); a region
+ * block id outside [0, num_blocks) or a row too short raises
+ * TA_ERR_BAD_PREFIX.  Same shape, workspace, outputs and tree sizes (up to 256
+ * nodes) as tree_attn_verify.  [pith.science verdict record: desk editor letter (paged
  * KV with tree padding) and referee summary (paged/persistent KV-cache
  * handling for tree attention)] */
 ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const void* k_cache,
@@ -235,7 +234,9 @@ ta_status tree_attn_commit_incache(const ta_shape* shape, const int32_t* parents
  * node i of sequence b (local index), draft_tokens[i] is the token the node
  * stands for and target_argmax[i] the target model's greedy next token at it
  * (both int32 [N], packed like the tree rows).  A root is accepted; node i is
- * accepted iff its parent p is and draft_tokens[i] == target_argmax[p].  The
+ * accepted iff its parent p is and draft_tokens[i] == target_argmax[p].  Trees
+ * of up to 64 nodes take one wave each, larger ones (up to 256) one 256-thread
+ * workgroup with multi-word ancestor sets.  The
  * accepted path ends at the deepest accepted node (the smallest index among
  * equally deep ones) and runs root first:
  *   accept_len[b]       number of path nodes (>= 1; 0 for an invalid tree)

@@ -124,18 +124,26 @@ def test_split_tokens_bounds():
 
 
 @pytest.mark.parametrize("T", [65, 200, 256])
-def test_large_trees_verify_and_split_only(T):
-    # trees of 65..256 nodes: the split path and the fused verify size a
-    # workspace (the verify gets as far as the workspace check: a null one is
-    # refused, not the shape); in-cache verify, acceptance and commit refuse
-    # the shape before touching any pointer
+def test_large_trees_accepted_by_every_entry_point(T):
+    # trees of 65..256 nodes: every entry point takes the shape and gets as
+    # far as its workspace check (a null workspace is refused, not the shape),
+    # before touching any device pointer
     s = shape(max_tree_nodes=T, total_tree_nodes=T)
     assert ta.workspace_size(s) > 0
     assert ta.split_tokens(s) > 0
     lib = load()
     assert lib.tree_attn_verify(ctypes.byref(s), *([FAKE] * 11), None, 1 << 40, None) == 4
-    assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), FAKE, 1 << 40, None) == 2
+    assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), None, 1 << 40, None) == 4
+    assert lib.tree_attn_accept_greedy(ctypes.byref(s), *([FAKE] * 7), None, 1 << 40, None) == 4
+    assert lib.tree_attn_commit_incache(ctypes.byref(s), *([FAKE] * 8), None, 1 << 40, None) == 4
+    assert lib.tree_attn_commit(ctypes.byref(s), *([FAKE] * 11), 4, FAKE, None, 1 << 40, None) == 4
+
+
+def test_trees_beyond_256_nodes_refused():
+    s = shape(max_tree_nodes=257, total_tree_nodes=257)
+    lib = load()
     assert lib.tree_attn_accept_greedy(ctypes.byref(s), *([FAKE] * 7), FAKE, 1 << 40, None) == 2
+    assert lib.tree_attn_verify_incache(ctypes.byref(s), *([FAKE] * 9), FAKE, 1 << 40, None) == 2
 
 
 def test_launch_info_mode_choice():

@@ -93,6 +93,43 @@ def test_accept_brute_force_random_trees():
         assert bonus[0] == argmax[want[-1]]
 
 
+def test_accept_brute_force_large_trees():
+    # trees of 65..256 nodes (forests too) with matching rates high enough for
+    # long accepted paths, against the brute force over every root path
+    from helpers import random_tree
+    rng = np.random.default_rng(12)
+    for k in range(12):
+        T = int(rng.integers(65, 257))
+        par = random_tree(rng, T, forest_p=0.05 if k % 3 == 0 else 0.0)
+        draft = rng.integers(0, 2, size=T)
+        argmax = rng.integers(0, 2, size=T)
+        if k % 2:   # mostly matching steps: paths run deep
+            par_arr = np.array(par)
+            draft = np.where(rng.random(T) < 0.9, argmax[np.maximum(par_arr, 0)], draft)
+        n, path, bonus = oracle.accept_greedy(np.array(par), np.array([0, T]), draft, argmax, 256)
+        want = _brute_force(par, draft, argmax)
+        assert list(path[0, :n[0]]) == want
+        assert np.all(path[0, n[0]:] == -1)
+        assert bonus[0] == argmax[want[-1]]
+
+
+def test_accept_chain_closed_form_256():
+    rng = np.random.default_rng(13)
+    T = 256
+    par = np.arange(-1, T - 1, dtype=np.int32)
+    for lead in (0, 63, 64, 200, 255):
+        argmax = rng.integers(0, 5, size=T)
+        draft = np.empty(T, dtype=np.int64)
+        draft[0] = 0
+        draft[1:] = argmax[:-1]                       # every step matches ...
+        if lead + 1 < T:
+            draft[lead + 1] = argmax[lead] + 1        # ... until step lead + 1
+        n, path, bonus = oracle.accept_greedy(par, np.array([0, T]), draft, argmax, T)
+        assert n[0] == 1 + lead
+        assert list(path[0, :n[0]]) == list(range(1 + lead))
+        assert bonus[0] == argmax[lead]
+
+
 def test_accept_packed_batch_matches_per_sequence():
     rng = np.random.default_rng(3)
     trees = [TREE_12, [-1], TREE_CHAIN4, TREE_12]

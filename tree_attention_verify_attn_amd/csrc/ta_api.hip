@@ -585,7 +585,6 @@ ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const v
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!prefix_lens || !tree_offsets || !block_table || !k_cache || !v_cache)
     return TA_ERR_INVALID_ARG;
   if (shape->num_blocks < 1) return TA_ERR_INVALID_ARG;
@@ -598,7 +597,7 @@ ta_status tree_attn_verify_incache(const ta_shape* shape, const void* q, const v
   Params p = base_params(shape, L, ws);
   // one-sequence numbering needs spare lanes in the block-id load for the tree
   // region's blocks (the region's position is known only with P)
-  if (L.chunk / kBlock + 2 > 64) p.single = 0;
+  if (L.chunk / kBlock + cdiv(shape->max_tree_nodes, kBlock) + 1 > 64) p.single = 0;
   p.tree_in_cache = 1;
   p.q = q;
   p.k_cache = k_cache;
@@ -619,7 +618,6 @@ ta_status tree_attn_commit_incache(const ta_shape* shape, const int32_t* parents
                                    size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens ||
       !k_cache || !v_cache)
     return TA_ERR_INVALID_ARG;
@@ -655,7 +653,6 @@ ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
                                   size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !bonus_token) return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!parents || !draft_tokens || !target_argmax))
     return TA_ERR_INVALID_ARG;
@@ -672,8 +669,12 @@ ta_status tree_attn_accept_greedy(const ta_shape* shape, const int32_t* parents,
   a.batch = shape->batch;
   a.total_nodes = shape->total_tree_nodes;
   a.max_tree = shape->max_tree_nodes;
-  hipLaunchKernelGGL(accept_kernel, dim3(unsigned(cdiv(shape->batch, kAcceptWaves))),
-                     dim3(64 * kAcceptWaves), 0, stream, a);
+  if (shape->max_tree_nodes <= kMaxTree)
+    hipLaunchKernelGGL(accept_kernel, dim3(unsigned(cdiv(shape->batch, kAcceptWaves))),
+                       dim3(64 * kAcceptWaves), 0, stream, a);
+  else  // multi-word ancestor sets: one 256-thread workgroup per tree
+    hipLaunchKernelGGL(accept_words_kernel, dim3(unsigned(shape->batch)), dim3(kMaxTreeSplit), 0,
+                       stream, a);
   return static_cast<ta_status>(launch_status());
 }
 
@@ -686,7 +687,6 @@ ta_status tree_attn_commit(const ta_shape* shape, const void* k_tree, const void
                            hipStream_t stream) {
   int st = check_shape(shape);
   if (st != kOk) return static_cast<ta_status>(st);
-  if (shape->max_tree_nodes > kMaxTree) return TA_ERR_UNSUPPORTED;  // one mask word
   if (!tree_offsets || !accept_len || !accept_path || !block_table || !prefix_lens)
     return TA_ERR_INVALID_ARG;
   if (shape->total_tree_nodes > 0 && (!parents || !k_tree || !v_tree)) return TA_ERR_INVALID_ARG;

@@ -89,7 +89,123 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) accept_kernel(AcceptParams 
   }
 }
 
+// Acceptance for trees of up to 256 nodes: one workgroup of 256 threads per
+// sequence, thread i = node i.  The ancestor-or-self sets are W = 4 words per
+// node, built by pointer jumping through LDS (eight rounds); the bad steps
+// of wave w form word w of the bad-step set (one ballot per wave, since a
+// wave covers nodes 64w .. 64w + 63).  A node is accepted when its set and
+// the bad-step set share no bit; the deepest accepted node (smallest index
+// among equally deep ones) wins a workgroup max over depth * 256 + (255 - i),
+// and its set, read in increasing node order, is the path root first.
+__global__ void __launch_bounds__(kMaxTreeSplit) accept_words_kernel(AcceptParams a) {
+  constexpr int W = kMaxTreeSplit / 64;
+  __shared__ uint64_t anc_sh[kMaxTreeSplit * W];
+  __shared__ int up_sh[kMaxTreeSplit];
+  __shared__ int amax_sh[kMaxTreeSplit];
+  __shared__ uint64_t badstep_sh[W];
+  __shared__ int key_sh[W];
+  __shared__ int bad_sh;
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int lane = i & 63;
+  const int w = i >> 6;
+  const int o0 = a.tree_offsets[b];
+  const int o1 = a.tree_offsets[b + 1];
+  const int T = o1 - o0;
+  int32_t* path = a.path + size_t(b) * a.max_tree;
+  const bool shape_ok = o0 >= 0 && o1 > o0 && o1 <= a.total_nodes && T <= a.max_tree;
+  // one memory trip for everything per node
+  int par = -1, draft = 0, amax = 0;
+  if (shape_ok && i < T) {
+    par = a.parents[o0 + i];
+    draft = a.draft[o0 + i];
+    amax = a.argmax[o0 + i];
+  }
+  const bool bad_i = shape_ok && i < T && !(par == -1 || (par >= 0 && par < i));
+  if (i == 0) bad_sh = 0;
+  __syncthreads();
+  if (bad_i) bad_sh = 1;
+  amax_sh[i] = amax;
+  int up = (shape_ok && i < T && !bad_i) ? par : -1;
+  uint64_t anc[W];
+#pragma unroll
+  for (int x = 0; x < W; ++x) anc[x] = (i < T && x == w) ? (uint64_t(1) << lane) : 0;
+  for (int round = 0; round < 8; ++round) {
+#pragma unroll
+    for (int x = 0; x < W; ++x) anc_sh[i * W + x] = anc[x];
+    up_sh[i] = up;
+    __syncthreads();
+    if (up >= 0) {
+#pragma unroll
+      for (int x = 0; x < W; ++x) anc[x] |= anc_sh[up * W + x];
+      up = up_sh[up];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < W; ++x) anc_sh[i * W + x] = anc[x];  // final sets (read below, after a barrier)
+  if (!shape_ok || bad_sh) {
+    if (i == 0) {
+      set_error(a.hdr, kErrBadTree);
+      a.accept_len[b] = 0;
+      a.bonus[b] = -1;
+    }
+    if (i < a.max_tree) path[i] = -1;
+    return;
+  }
+  const bool good = i < T && (par < 0 || draft == amax_sh[par]);
+  const uint64_t bad_steps = __ballot(i < T && !good);  // word w of the bad-step set
+  if (lane == 0) badstep_sh[w] = bad_steps;
+  __syncthreads();
+  bool accepted = i < T;
+  int depth = -1;
+#pragma unroll
+  for (int x = 0; x < W; ++x) {
+    accepted = accepted && (anc[x] & badstep_sh[x]) == 0;
+    depth += __popcll(anc[x]);
+  }
+  int key = accepted ? depth * kMaxTreeSplit + (kMaxTreeSplit - 1 - i) : -1;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) key = max(key, __shfl_xor(key, d));
+  if (lane == 0) key_sh[w] = key;
+  __syncthreads();
+  key = max(max(key_sh[0], key_sh[1]), max(key_sh[2], key_sh[3]));
+  const int last = kMaxTreeSplit - 1 - (key % kMaxTreeSplit);  // a root is always accepted
+  // the path: node i is on it iff bit i of last's set is set; its place is the
+  // number of path nodes below it
+  const uint64_t mine = anc_sh[last * W + w];
+  int below = __popcll(mine & ((uint64_t(1) << lane) - 1));
+  int n = 0;
+#pragma unroll
+  for (int x = 0; x < W; ++x) {
+    const int c = __popcll(anc_sh[last * W + x]);
+    below += x < w ? c : 0;
+    n += c;
+  }
+  if (i < a.max_tree && i >= n) path[i] = -1;
+  if ((mine >> lane) & 1) path[below] = i;
+  if (i == 0) {
+    a.accept_len[b] = n;
+    a.bonus[b] = amax_sh[last];
+  }
+}
+
 // ------------------------------------------------------------------ commit
+// This lane's share of the check that path[0..A) is a root path of a tree of
+// T nodes: step t (lanes t = lane, lane + 64, ...) goes from path[t - 1] (no
+// parent for t = 0) to a child of it.  The caller takes the wave's AND.
+__device__ __forceinline__ bool path_steps_ok(const int32_t* path, const int32_t* parents, int A,
+                                              int T) {
+  const int lane = threadIdx.x & 63;
+  bool ok = true;
+  for (int t = lane; t < A; t += 64) {
+    const int node = path[t];
+    const int prev = t == 0 ? -1 : path[t - 1];
+    ok = ok && node >= 0 && node < T && parents[node] == prev;
+  }
+  return ok;
+}
+
 struct CommitPlan {  // per sequence, in the workspace
   int P;     // prefix length before the commit
   int A;     // rows to append (0 when the sequence is skipped)
@@ -116,7 +232,8 @@ struct CommitParams {
 };
 
 // 1. one wave per sequence: lane t checks that path step t goes from the
-// previous node (or from "no parent" for t = 0) to a child of it.
+// previous node (or from "no parent" for t = 0) to a child of it, 64 steps
+// at a time.
 __global__ void __launch_bounds__(64 * kAcceptWaves) commit_check_kernel(CommitParams c) {
   const int b = blockIdx.x * kAcceptWaves + int(threadIdx.x >> 6);
   if (b >= c.batch) return;
@@ -127,12 +244,7 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) commit_check_kernel(CommitP
   const int A = c.accept_len[b];
   const int P = c.prefix_lens[b];
   bool ok = o0 >= 0 && o1 > o0 && o1 <= c.total_nodes && T <= c.max_tree && A >= 0 && A <= T;
-  const bool mine = ok && lane < A;
-  const int node = mine ? c.path[size_t(b) * c.max_tree + lane] : -1;
-  const int prev = __shfl_up(node, 1);
-  bool step_ok = true;
-  if (mine) step_ok = node >= 0 && node < T && c.parents[o0 + node] == (lane == 0 ? -1 : prev);
-  ok = ok && __all(step_ok);
+  ok = ok && __all(path_steps_ok(c.path + size_t(b) * c.max_tree, c.parents + (ok ? o0 : 0), ok ? A : 0, T));
   const bool p_ok = P >= 0 && P <= kBlock * c.max_blocks;
   if (lane == 0) {
     if (!ok) set_error(c.hdr, kErrBadTree);
@@ -242,7 +354,8 @@ __global__ void __launch_bounds__(kThreads) commit_apply_kernel(CommitParams c) 
 // The tree's rows already sit at cache positions P .. P+T-1 (the "tree
 // padding" layout: paged KV with the tree after the prefix, pith.science
 // verdict record, desk editor letter).  One workgroup per sequence: wave 0
-// checks the path and the region's (at most two) block ids; then the
+// checks the path and the region's block ids (at most kRegionBlocks: a region
+// of up to 256 rows starting anywhere in a block); then the
 // accepted rows are compacted in place -- position P + t takes the row at
 // P + path[t] -- in rounds of 8 x 16 bytes per thread, all loads of a round
 // before any of its stores.  Row chunks are numbered t-major and path[t] >= t
@@ -262,7 +375,7 @@ struct IncacheParams {
 };
 
 __global__ void __launch_bounds__(kThreads) commit_incache_kernel(IncacheParams c) {
-  __shared__ int sh[5];  // ok, P, A, first block, second block
+  __shared__ int sh[3 + kRegionBlocks];  // ok, P, A, the region's blocks
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -273,34 +386,24 @@ __global__ void __launch_bounds__(kThreads) commit_incache_kernel(IncacheParams 
     const int A = c.accept_len[b];
     const int P = c.prefix_lens[b];
     bool ok = o0 >= 0 && o1 > o0 && o1 <= c.total_nodes && T <= c.max_tree && A >= 0 && A <= T;
-    const bool mine = ok && lane < A;
-    const int node = mine ? c.path[size_t(b) * c.max_tree + lane] : -1;
-    const int prev = __shfl_up(node, 1);
-    bool step_ok = true;
-    if (mine) step_ok = node >= 0 && node < T && c.parents[o0 + node] == (lane == 0 ? -1 : prev);
-    ok = ok && __all(step_ok);
-    const bool p_ok = P >= 0 && P + T <= kBlock * c.max_blocks;
+    ok = ok && __all(path_steps_ok(c.path + size_t(b) * c.max_tree, c.parents + (ok ? o0 : 0), ok ? A : 0, T));
+    const bool p_ok = ok && P >= 0 && P + T <= kBlock * c.max_blocks;
+    const int nreg = p_ok ? (P + T - 1) / kBlock - P / kBlock + 1 : 0;  // <= kRegionBlocks
     int blk = 0;
-    if (p_ok && lane < 2 && P / kBlock + lane < c.max_blocks)
-      blk = c.block_table[size_t(b) * c.max_blocks + P / kBlock + lane];
-    const int blk0 = __shfl(blk, 0);
-    const int blk1 = __shfl(blk, 1);
-    const bool two = p_ok && (P + T - 1) / kBlock > P / kBlock;
-    const bool blk_ok = p_ok && blk0 >= 0 && blk0 < c.num_blocks &&
-                        (!two || (blk1 >= 0 && blk1 < c.num_blocks));
+    if (lane < nreg) blk = c.block_table[size_t(b) * c.max_blocks + P / kBlock + lane];
+    const bool blk_ok = p_ok && __all(lane >= nreg || (blk >= 0 && blk < c.num_blocks));
     if (lane == 0) {
       if (!ok) set_error(c.hdr, kErrBadTree);
       else if (!blk_ok) set_error(c.hdr, kErrBadPrefix);
       sh[0] = ok && blk_ok;
       sh[1] = P;
       sh[2] = A;
-      sh[3] = blk0;
-      sh[4] = blk1;
     }
+    if (lane < kRegionBlocks) sh[3 + lane] = blk;
   }
   __syncthreads();
   if (!sh[0]) return;
-  const int P = sh[1], A = sh[2], blk0 = sh[3], blk1 = sh[4];
+  const int P = sh[1], A = sh[2];
   const int chunks = c.row_bytes / 16;
   const int per_t = c.hkv * chunks;
   const int total = A * per_t;
@@ -308,7 +411,7 @@ __global__ void __launch_bounds__(kThreads) commit_incache_kernel(IncacheParams 
   unsigned char* kc = static_cast<unsigned char*>(c.k_cache);
   unsigned char* vc = static_cast<unsigned char*>(c.v_cache);
   auto addr = [&](int pos, int g, int ch) {
-    const int blk = pos / kBlock == P / kBlock ? blk0 : blk1;
+    const int blk = sh[3 + pos / kBlock - P / kBlock];
     return ((size_t(blk) * c.hkv + g) * kBlock + pos % kBlock) * c.row_bytes + size_t(ch) * 16;
   };
   for (int base = 0; base < total; base += kThreads * kPer) {

@@ -414,8 +414,10 @@ struct Geo {
 constexpr int kHidSense = 0;                  // the group's sense word (thread 0)
 constexpr int kHidOff = 1;                    // tree_offsets[0], [1] (wave 0, lanes 0 and 1)
 constexpr int kHidP = 4;                      // the prefix length, per wave
-constexpr int kHidBlk = kHidP + kAttnWaves;   // two tree-region block ids, per wave
-constexpr int kHidStarted = kHidBlk + 2 * kAttnWaves;  // the group's started count (thread 0)
+// blocks a tree region (cache positions P .. P+T-1, T <= 256) can touch
+constexpr int kRegionBlocks = kMaxTreeSplit / kBlock + 1;
+constexpr int kHidBlk = kHidP + kAttnWaves;   // the tree region's block ids, per wave
+constexpr int kHidStarted = kHidBlk + kRegionBlocks * kAttnWaves;  // the group's started count (thread 0)
 constexpr int kHidWords = kHidStarted + 1;
 
 struct SmemMisc {
@@ -708,18 +710,19 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   if (FUSED && (BIG ? tid < kMaxTreeSplit : w == 0) && (need_p || it.s == si.S - 1))
     par = p.parents[si.off + min(BIG ? tid : lane, si.T - 1)];
   // tree rows kept in the cache right after the prefix (positions P .. P+T-1,
-  // at most two blocks).  The region starts inside this chunk's block range
-  // or right after it, so two more lanes of the block-id load below cover its
-  // blocks (lanes cpb and cpb + 1 of the id vector), also before P is known.
-  // When a chunk spans 63 or 64 blocks there are no spare lanes: lanes 0 and
-  // 1 of every wave then read the two ids (such launches use the sequence
-  // table, so P is known here).
+  // at most nreg_max = T_max / 64 + 1 blocks).  The region starts inside this
+  // chunk's block range or right after it, so nreg_max more lanes of the
+  // block-id load below cover its blocks (lanes cpb .. cpb + nreg_max - 1 of
+  // the id vector), also before P is known.  When the chunk leaves too few
+  // spare lanes, lanes 0 .. nreg_max - 1 of every wave read the region's ids
+  // (such launches use the sequence table, so P is known here).
   const int cpb = it.chunk / kBlock;  // blocks per chunk
-  const bool extra_lanes = FUSED && p.tree_in_cache && cpb + 2 <= 64;
+  const int nreg_max = cdiv(p.max_tree, kBlock) + 1;
+  const bool extra_lanes = FUSED && p.tree_in_cache && cpb + nreg_max <= 64;
   const bool tree_blk_here = FUSED && p.tree_in_cache && !extra_lanes && it.s == si.S - 1;
-  if (tree_blk_here && lane < 2)
+  if (tree_blk_here && lane < nreg_max)
     hidden_load(p.block_table + size_t(it.b) * p.max_blocks + min(si.P / kBlock + lane, p.max_blocks - 1),
-                &sm.hid[kHidBlk + 2 * w]);
+                &sm.hid[kHidBlk + kRegionBlocks * w]);
   // one-sequence numbering: the prefix length, and (first item only) the two
   // tree offsets, which must be 0 and N
   const bool first_of_launch = it.s == 0 && it.g == 0 && it.rp == 0;
@@ -730,7 +733,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   int my_id = -1;
   if constexpr (!SUFFIX) {
     const int lb = it.s * cpb + lane;
-    if (lane < cpb + (extra_lanes ? 2 : 0) && lb < p.max_blocks)
+    if (lane < cpb + (extra_lanes ? nreg_max : 0) && lb < p.max_blocks)
       my_id = p.block_table[size_t(it.b) * p.max_blocks + lb];
   }
   // suffix: this lane's row's mask words, one per 64-node segment
@@ -747,7 +750,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
   wait_vm<0>();
   const unsigned sense0 = tid == 0 ? unsigned(sm.hid[kHidSense]) : 0u;  // used by thread 0 only
-  const int tree_blk = tree_blk_here && lane < 2 ? sm.hid[kHidBlk + 2 * w + lane] : 0;
+  const int tree_blk = tree_blk_here && lane < nreg_max ? sm.hid[kHidBlk + kRegionBlocks * w + lane] : 0;
   if (need_p) {
     const int p_read = __builtin_amdgcn_readfirstlane(sm.hid[kHidP + w]);  // the same in every lane
     const int toff = first_of_launch && w == 0 && lane < 2 ? sm.hid[kHidOff + lane] : 0;
@@ -781,30 +784,29 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   unsigned char* tk = tree_lds;
   unsigned char* tv = tree_lds + p.tree_lds_half;
   const int tree_rows = (SUFFIX || big) ? kBlock : p.tree_lds_half / ROWB;  // staged rows (>= tree size)
+  // in-cache rows: the region's block ids, lane k holding block k of the
+  // region (checked; bad ids are flagged and read as block 0)
+  int regv = 0;
+  if (with_tree && p.tree_in_cache) {
+    const int nreg = (si.P + si.T - 1) / kBlock - si.P / kBlock + 1;
+    if (extra_lanes) {
+      const int r0 = si.P / kBlock - it.s * cpb;  // 0 .. cpb
+      regv = __shfl(my_id, min(r0 + lane, 63));
+    } else {
+      regv = tree_blk;
+    }
+    const bool ok = (si.P + si.T - 1) / kBlock < p.max_blocks &&
+                    __all(lane >= nreg || (regv >= 0 && regv < p.num_blocks));
+    if (!ok) {
+      if (tid == 0) set_error(p.hdr, kErrBadPrefix);
+      regv = 0;
+    }
+  }
+  // block of cache position pos of the region (wave-wide shuffle)
+  auto region_block = [&](int pos) { return __shfl(regv, pos / kBlock - si.P / kBlock); };
   if (with_tree && !big) {
     const int Tn = si.T;
     const int ninstr = p.tree_lds_half / 1024;
-    // in-cache rows: the region's two block ids (checked; a bad one is
-    // flagged and read as block 0)
-    int blk0 = 0, blk1 = 0;
-    if (p.tree_in_cache) {
-      if (extra_lanes) {
-        const int r0 = si.P / kBlock - it.s * cpb;  // 0 .. cpb
-        blk0 = __shfl(my_id, r0);
-        blk1 = __shfl(my_id, r0 + 1);
-      } else {
-        blk0 = __shfl(tree_blk, 0);
-        blk1 = __shfl(tree_blk, 1);
-      }
-      const int last_idx = (si.P + Tn - 1) / kBlock;
-      const bool two = last_idx > si.P / kBlock;
-      const bool ok = last_idx < p.max_blocks && blk0 >= 0 && blk0 < p.num_blocks &&
-                      (!two || (blk1 >= 0 && blk1 < p.num_blocks));
-      if (!ok) {
-        if (tid == 0) set_error(p.hdr, kErrBadPrefix);
-        blk0 = blk1 = 0;
-      }
-    }
     for (int m = w; m < ninstr; m += kAttnWaves) {
       const int u = m * 64 + lane;
       const int t = min(u / KCH, Tn - 1);
@@ -815,7 +817,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       const T* vb;
       if (p.tree_in_cache) {
         const int pos = si.P + t;
-        const int blk = (pos / kBlock == si.P / kBlock) ? blk0 : blk1;
+        const int blk = region_block(pos);
         roff = ((size_t(blk) * p.hkv + it.g) * kBlock + (pos % kBlock)) * D;
         kb = static_cast<const T*>(p.k_cache);
         vb = static_cast<const T*>(p.v_cache);
@@ -860,8 +862,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // the item's KV blocks (ring unit nblk + segment): in the split path's
   // suffix mode, and in the fused kernel's last chunk for trees of more than
   // 64 nodes.  Each stages the segment's rows, clamped to the last node,
-  // gathered from the [node, KV head, D] tree tensors: KI transfers per wave
-  // and tensor, like a KV block.
+  // gathered from the [node, KV head, D] tree tensors, or from the cache
+  // positions P + node when the tree rows sit in the cache: KI transfers per
+  // wave and tensor, like a KV block.
   const int nseg = (SUFFIX || (with_tree && big)) ? cdiv(si.T, kBlock) : 0;
   const int ntot = nblk + nseg;  // ring units of the item
   auto stage = [&](int j, int sl) {
@@ -872,11 +875,21 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
       const int t = min(kBlock * sg + u / KCH, si.T - 1);
       const int pc = u % KCH;
       const int c = pc ^ swz_key<T, D>(u / KCH);
-      const size_t roff = (size_t(si.off + t) * p.hkv + it.g) * D;
-      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.k_tree) + roff) + c * 16,
-                sk + m * 1024);
-      lds_dma16(reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.v_tree) + roff) + c * 16,
-                sk + BLKB + m * 1024);
+      size_t roff;
+      const T* kb;
+      const T* vb;
+      if (FUSED && p.tree_in_cache) {
+        const int pos = si.P + t;
+        roff = ((size_t(region_block(pos)) * p.hkv + it.g) * kBlock + (pos % kBlock)) * D;
+        kb = static_cast<const T*>(p.k_cache);
+        vb = static_cast<const T*>(p.v_cache);
+      } else {
+        roff = (size_t(si.off + t) * p.hkv + it.g) * D;
+        kb = static_cast<const T*>(p.k_tree);
+        vb = static_cast<const T*>(p.v_tree);
+      }
+      lds_dma16(reinterpret_cast<const unsigned char*>(kb + roff) + c * 16, sk + m * 1024);
+      lds_dma16(reinterpret_cast<const unsigned char*>(vb + roff) + c * 16, sk + BLKB + m * 1024);
     }
   };
   auto issue_any = [&](int j, int sl) {
