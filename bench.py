@@ -49,8 +49,12 @@ PEAK_F32_TFLOPS = 157.3   # dense fp32 matrix peak
 # counter-measured HBM traffic of the fused kernel, per workload (see profiles/)
 TRAFFIC_FILES = {
     2: os.path.join(ROOT, "profiles", "attn_kernel_llama8b_verify_8k_traffic.json"),
+    3: os.path.join(ROOT, "profiles", "attn_kernel_70b_head_share_b32_traffic.json"),
+    4: os.path.join(ROOT, "profiles", "attn_kernel_maverick_head_share_8k_traffic.json"),
     5: os.path.join(ROOT, "profiles", "attn_kernel_ragged_b256_traffic.json"),
 }
+# counter-measured MFMA busy cycles and bf16 MFMA work of the fused kernel (see profiles/)
+MFMA_FILE = os.path.join(ROOT, "profiles", "attn_kernel_mfma_counters.json")
 
 
 def log(msg: str) -> None:
@@ -116,6 +120,20 @@ def measured_traffic(config_index: int, split: int):
     if rec.get("config") != config_index or rec.get("split_tokens") != split:
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_mfma(config_index: int, split: int):
+    """(counted MFMA utilisation, counted bf16 MFMA flops) of the fused kernel
+    from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources and the same workload; else (None, None)."""
+    try:
+        with open(MFMA_FILE) as f:
+            rec = json.load(f).get(str(config_index))
+    except (OSError, ValueError):
+        return None, None
+    if not rec or rec.get("kernel_sha") != kernel_source_hash() or rec.get("split_tokens") != split:
+        return None, None
+    return rec.get("mfma_util_counted"), rec.get("mfma_flops_counted")
 
 
 def cpu_model() -> str:
@@ -545,6 +563,8 @@ def main() -> int:
 
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.config, split) if args.entry == "verify" else None
+    mfma_counted, mfma_flops = (measured_mfma(args.config, split) if args.entry == "verify"
+                                else (None, None))
     # the roofline that bounds this workload: HBM unless its matrix work takes
     # longer at peak than its algorithmic bytes do (large trees, long prefixes)
     peak_tf = PEAK_BF16_TFLOPS if inp.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -598,6 +618,8 @@ def main() -> int:
                        if args.entry in ("verify", "incache")
                        else "split path: mask + prefix + suffix + merge kernels"),
             "mfma_util": round(achieved_tf / peak_tf, 5),
+            "mfma_util_counted": mfma_counted,
+            "mfma_flops_counted": mfma_flops,
         },
         "host_wall_s": round(t_host, 3),
     }
