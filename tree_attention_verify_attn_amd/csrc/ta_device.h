@@ -56,15 +56,44 @@ __device__ __forceinline__ float sum_over_quads(float v) {
                                                   __builtin_bit_cast(unsigned, v), false, false);
   return __builtin_bit_cast(float, unsigned(b[0])) + __builtin_bit_cast(float, unsigned(b[1]));
 }
-// Reductions over a 32-lane half-wave.
-__device__ __forceinline__ float max_over_32(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 32));
-  return v;
+// Integer sum, max and inclusive prefix sum over the 64 lanes of a wave, on
+// the VALU with no LDS round trip: DPP steps within each row of 16 lanes
+// (rotations by 8, 4, 2, 1 for the reductions, so every lane of a row ends
+// with the row's result; shifts by 1, 2, 4, 8 for the prefix sum), then
+// across rows the lane swaps l ^ 16 and l ^ 32 (reductions) or the row
+// broadcasts of lanes 15 and 31 (prefix sum).  Every lane of the wave must be
+// active.
+constexpr int kDppRowShr = 0x110;    // + n: lane l of a row reads lane l - n (0 outside the row)
+constexpr int kDppRowRor = 0x120;    // + n: lane l of a row reads lane (l - n) mod 16
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowRor + 8, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowRor + 4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowRor + 2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowRor + 1, 0xf, 0xf, false);
+  const auto a = __builtin_amdgcn_permlane16_swap(unsigned(v), unsigned(v), false, false);
+  v = int(a[0]) + int(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(unsigned(v), unsigned(v), false, false);
+  return int(b[0]) + int(b[1]);
 }
-__device__ __forceinline__ float sum_over_32(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 32);
+__device__ __forceinline__ int wave_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowRor + 8, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowRor + 4, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowRor + 2, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowRor + 1, 0xf, 0xf, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(unsigned(v), unsigned(v), false, false);
+  v = max(int(a[0]), int(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(unsigned(v), unsigned(v), false, false);
+  return max(int(b[0]), int(b[1]));
+}
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 8, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);  // rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);  // rows 2 and 3
   return v;
 }
 

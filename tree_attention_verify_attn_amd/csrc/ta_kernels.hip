@@ -109,12 +109,7 @@ constexpr int kSeqBits = 11;        // sequence index bits in a sort key (batch 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(inc, d);
-    if (lane >= d) inc += t;
-  }
+  const int inc = wave_inclusive_sum(v);
   if (lane == 63) scratch[w] = inc;
   __syncthreads();
   int before = 0;
@@ -134,12 +129,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
 __device__ __forceinline__ void block_sum2_max(int& a, int& b, int& c, int* scratch) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    a += __shfl_xor(a, d);
-    b += __shfl_xor(b, d);
-    c = max(c, __shfl_xor(c, d));
-  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_max(c);
   if (lane == 0) {
     scratch[w] = a;
     scratch[kAttnWaves + w] = b;
