@@ -91,7 +91,8 @@ __global__ void __launch_bounds__(64 * kAcceptWaves) accept_kernel(AcceptParams 
 
 // Acceptance for trees of up to 256 nodes: one workgroup of 256 threads per
 // sequence, thread i = node i.  The ancestor-or-self sets are W = 4 words per
-// node, built by pointer jumping through LDS (eight rounds); the bad steps
+// node, built by pointer jumping through LDS (at most eight rounds; it stops
+// once no node has an ancestor link left); the bad steps
 // of wave w form word w of the bad-step set (one ballot per wave, since a
 // wave covers nodes 64w .. 64w + 63).  A node is accepted when its set and
 // the bad-step set share no bit; the deepest accepted node (smallest index
@@ -101,6 +102,7 @@ __global__ void __launch_bounds__(kMaxTreeSplit) accept_words_kernel(AcceptParam
   constexpr int W = kMaxTreeSplit / 64;
   __shared__ uint64_t anc_sh[kMaxTreeSplit * W];
   __shared__ int up_sh[kMaxTreeSplit];
+  __shared__ int more_sh[2];  // some node still had a link after round r (slot r & 1)
   __shared__ int amax_sh[kMaxTreeSplit];
   __shared__ uint64_t badstep_sh[W];
   __shared__ int key_sh[W];
@@ -134,13 +136,16 @@ __global__ void __launch_bounds__(kMaxTreeSplit) accept_words_kernel(AcceptParam
 #pragma unroll
     for (int x = 0; x < W; ++x) anc_sh[i * W + x] = anc[x];
     up_sh[i] = up;
+    if (i == 0) more_sh[round & 1] = 0;
     __syncthreads();
     if (up >= 0) {
 #pragma unroll
       for (int x = 0; x < W; ++x) anc[x] |= anc_sh[up * W + x];
       up = up_sh[up];
+      if (up >= 0) more_sh[round & 1] = 1;
     }
     __syncthreads();
+    if (more_sh[round & 1] == 0) break;  // no node has a link left
   }
 #pragma unroll
   for (int x = 0; x < W; ++x) anc_sh[i * W + x] = anc[x];  // final sets (read below, after a barrier)

@@ -417,6 +417,7 @@ struct SmemMisc {
   int hid[kHidWords];
   int scratch[kAttnThreads];
   int bcast[4];
+  int more[2];             // pointer jumping: some node still had a link after round r (slot r & 1)
   float half_m[kMaxTree];  // running max / sum of the upper key half, per row
   float half_l[kMaxTree];
 };
@@ -894,8 +895,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // tree mask by pointer jumping (as in tree_mask_wave)
   if (with_tree && big) {
     // node i (thread i) keeps its ancestor-or-self set in kSegMax words and a
-    // link to an ancestor; eight rounds through LDS OR in the linked node's
-    // set and follow its link.  Words of node i end at bw[i * kSegMax ..].
+    // link to an ancestor; rounds through LDS OR in the linked node's set and
+    // follow its link, until no node has a link left (at most eight rounds).
+    // Words of node i end at bw[i * kSegMax ..].
     uint64_t* bw = reinterpret_cast<uint64_t*>(tree_lds);
     int* bup = reinterpret_cast<int*>(tree_lds + kMaxTreeSplit * kSegMax * sizeof(uint64_t));
     const int Tn = si.T;
@@ -912,13 +914,19 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
         for (int x = 0; x < kSegMax; ++x) bw[tid * kSegMax + x] = anc[x];
         bup[tid] = up;
       }
+      if (tid == 0) sm.more[round & 1] = 0;
       __syncthreads();
       if (node && up >= 0) {
 #pragma unroll
         for (int x = 0; x < kSegMax; ++x) anc[x] |= bw[up * kSegMax + x];
         up = bup[up];
+        if (up >= 0) sm.more[round & 1] = 1;
       }
       __syncthreads();
+      // no node has a link left: every set is complete (the other slot is
+      // cleared only after the next round's first barrier, so all threads
+      // read this one before it changes)
+      if (sm.more[round & 1] == 0) break;
     }
     if (node) {
 #pragma unroll
@@ -1614,12 +1622,14 @@ __global__ void __launch_bounds__(64) mask_kernel(Params p, uint64_t* mask_out) 
 
 // One workgroup of 256 threads per sequence for trees of up to 256 nodes:
 // thread i keeps node i's ancestor-or-self set in W <= 4 words and a link
-// to an ancestor; each of eight rounds ORs in the set of the linked node and
-// follows its link (through LDS), doubling the distance covered.  Output
+// to an ancestor; each round ORs in the set of the linked node and follows
+// its link (through LDS), doubling the distance covered, until no node has a
+// link left (at most eight rounds).  Output
 // mask_out[(off + i) * W + w], bit j % 64 of word j / 64.
 __global__ void __launch_bounds__(kMaxTreeSplit) mask_words_kernel(Params p, uint64_t* mask_out) {
   __shared__ uint64_t anc_sh[kMaxTreeSplit * 4];
   __shared__ int up_sh[kMaxTreeSplit];
+  __shared__ int more_sh[2];  // some node still had a link after round r (slot r & 1)
   __shared__ int bad_sh;
   const int b = blockIdx.x;
   const int i = threadIdx.x;
@@ -1649,13 +1659,16 @@ __global__ void __launch_bounds__(kMaxTreeSplit) mask_words_kernel(Params p, uin
 #pragma unroll
     for (int w = 0; w < 4; ++w) anc_sh[i * 4 + w] = anc[w];
     up_sh[i] = up;
+    if (i == 0) more_sh[round & 1] = 0;
     __syncthreads();
     if (up >= 0) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) anc[w] |= anc_sh[up * 4 + w];
       up = up_sh[up];
+      if (up >= 0) more_sh[round & 1] = 1;
     }
     __syncthreads();
+    if (more_sh[round & 1] == 0) break;  // no node has a link left
   }
   const bool bad = bad_sh != 0;
   if (bad && i == 0) set_error(p.hdr, kErrBadTree);
