@@ -19,7 +19,7 @@ constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
-constexpr int kMaxRingSlots = 3;       // KV blocks the attention kernel keeps in LDS
+constexpr int kMaxRingSlots = 2;       // KV blocks the attention kernel keeps in LDS
 constexpr int kMaxChunk = 4096;        // prefix tokens per work item, at most
 
 // Status codes, identical to ta_status in include/tree_attn.h.
