@@ -107,6 +107,42 @@ def test_fused_verify_large_trees_matches_oracle(dtype, D):
     assert_close_lse(host(lse), l_want, tol_l, "fused big-tree lse")
 
 
+def test_deep_chains_every_pointer_jumping_round():
+    # Chains are the deepest trees: a 256-node chain needs all eight
+    # pointer-jumping rounds (a link reaches 2^k ancestors after round k), a
+    # 129-node chain exactly eight, a 128-node chain seven.  The rounds stop
+    # early once no node has a link left, so these pin the last round in the
+    # mask kernel, the split path and the fused verify (one launch with all
+    # three, and one sequence with the 256-node chain alone).
+    import tree_attention_verify_attn_amd as ta
+    chains = [list(range(-1, 255)), list(range(-1, 128)), list(range(-1, 127))]
+    inp = _big(97, chains, [130, 0, 700])
+    d = to_device(inp, max_tree_nodes=256)
+    say("deep chains of 256, 129 and 128 nodes: masks, split path, fused verify")
+    mask = ta.build_mask(d.shape, d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64), oracle.build_masks_words(inp, 4))
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    out, lse, _ = run_split(d)
+    assert ta.get_error(d.workspace) == 0
+    assert_close(host(out), o_want, tol_o, "deep chains, split path o")
+    assert_close_lse(host(lse), l_want, tol_l, "deep chains, split path lse")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    assert_close(host(out), o_want, tol_o, "deep chains, fused o")
+    assert_close_lse(host(lse), l_want, tol_l, "deep chains, fused lse")
+    one = _big(98, [chains[0]], [2000], Hq=8, Hkv=2)
+    d1 = to_device(one, max_tree_nodes=256, split_tokens=512)
+    say("deep chain of 256 nodes, one sequence in 4 chunks")
+    out, lse = run_verify(d1)
+    assert ta.get_error(d1.workspace) == 0
+    o_want, l_want, _ = oracle.verify(one)
+    assert_close(host(out), o_want, tol_o, "deep chain one sequence o")
+    assert_close_lse(host(lse), l_want, tol_l, "deep chain one sequence lse")
+
+
 def test_fused_verify_large_tree_one_sequence_split_chunks():
     # one sequence (numbered without a table), a 256-node tree over a
     # 4000-token prefix cut into many chunks; small trees mixed in are covered

@@ -30,9 +30,12 @@ def _host_bits(x):
 
 
 def _large_trees(seed):
+    # the last one, a 256-node chain, is the deepest tree: its ancestor sets
+    # take all eight pointer-jumping rounds and its whole-path commit moves
+    # 256 rows
     rng = np.random.default_rng(seed)
     return [random_tree(rng, 200), list(range(-1, 99)), [-1] + [0] * 64,
-            random_tree(rng, 256, forest_p=0.05), random_tree(rng, 70)]
+            random_tree(rng, 256, forest_p=0.05), random_tree(rng, 70), list(range(-1, 255))]
 
 
 def _incache(seed, trees, lens, *, dtype="bf16", Hq=8, Hkv=2, D=128):
@@ -59,7 +62,7 @@ def _verify_incache(d):
 def test_verify_incache_large_trees_matches_oracle(dtype, D):
     import tree_attention_verify_attn_amd as ta
     # P = 63 under the 256-node tree: its region touches 5 blocks
-    inp, ic = _incache(401, _large_trees(4), [130, 1, 0, 63, 64], dtype=dtype, D=D)
+    inp, ic = _incache(401, _large_trees(4), [130, 1, 0, 63, 64, 100], dtype=dtype, D=D)
     d = to_device(ic, max_tree_nodes=256)
     say(f"verify_incache large trees {dtype} D={D}: {ta.launch_info(d.shape)}")
     out, lse = _verify_incache(d)
@@ -88,7 +91,7 @@ def test_verify_incache_large_tree_one_sequence(split):
 
 
 def test_verify_incache_large_equals_separate_buffers():
-    inp, ic = _incache(403, _large_trees(5), [700, 63, 5, 128, 1])
+    inp, ic = _incache(403, _large_trees(5), [700, 63, 5, 128, 1, 64])
     say("verify_incache vs separate tree rows, large trees")
     out_ic, lse_ic = _verify_incache(to_device(ic, max_tree_nodes=256))
     out_sep, lse_sep = run_verify(to_device(inp, max_tree_nodes=256))
@@ -159,7 +162,7 @@ def test_commit_large_trees_bit_exact(p_match):
     rng = np.random.default_rng(420)
     trees = _large_trees(6)
     inp = make_inputs(dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=128,
-                      prefix_lens=[63, 0, 200, 64, 1], trees=trees, rng=rng, spare_blocks=30,
+                      prefix_lens=[63, 0, 200, 64, 1, 20], trees=trees, rng=rng, spare_blocks=40,
                       extra_table_cols=5)
     draft, argmax = make_tokens(inp.parents, inp.tree_offsets, rng, p_match=p_match, vocab=5)
     free = free_list(inp, rng)
@@ -187,7 +190,7 @@ def test_commit_incache_large_trees_bit_exact(p_match):
     rng = np.random.default_rng(430)
     trees = _large_trees(7)
     inp = make_inputs(dtype="bf16", num_q_heads=8, num_kv_heads=4, head_dim=128,
-                      prefix_lens=[63, 64, 0, 63, 130], trees=trees, rng=rng, spare_blocks=30,
+                      prefix_lens=[63, 64, 0, 63, 130, 1], trees=trees, rng=rng, spare_blocks=40,
                       extra_table_cols=5)
     draft, argmax = make_tokens(inp.parents, inp.tree_offsets, rng, p_match=p_match, vocab=4)
     n, path, _ = oracle.accept_greedy(inp.parents, inp.tree_offsets, draft, argmax, 256)
