@@ -230,10 +230,47 @@ def floor_run(torch, nbytes: int, steps: int, replica_bytes: float) -> dict:
     read_us = timed(lambda r: torch.sum(src[r], dtype=torch.float32))
     copy_us = timed(lambda r: dst[r].copy_(src[r]))
     empty_us = timed(lambda r: torch.cuda._sleep(0))
+    # the measurement library's streaming read (libtafloor.so): the same bytes
+    # (rounded down to 16), read once and folded, for a few launch shapes
+    lib = floor_lib()
+    nb16 = (2 * n) // 16 * 16
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def stream_read(grid, threads, loads):
+        def fn(r):
+            rc = lib.ta_floor_read(ctypes.c_void_p(src[r].data_ptr()), nb16, grid, threads, loads,
+                                   ctypes.c_void_p(sink.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"ta_floor_read failed ({rc})")
+        return timed(fn)
+
+    shapes = {"256x512x4": (256, 512, 4), "1024x512x4": (1024, 512, 4),
+              "4096x512x4": (4096, 512, 4), "2048x256x8": (2048, 256, 8)}
+    sr = {k: round(stream_read(*v), 3) for k, v in shapes.items()}
+    best = min(sr, key=sr.get)
     return {"floor_bytes": 2 * n, "replicas": R, "steps": steps,
+            "stream_read_bytes": nb16,
+            "stream_read_us": sr,
+            "stream_read_best_us": sr[best], "stream_read_best_shape": best,
+            "stream_read_best_GBps": round(nb16 / sr[best] / 1e3, 1),
+            "stream_read_one_wg_per_cu_GBps": round(nb16 / sr["256x512x4"] / 1e3, 1),
             "sum_read_us": round(read_us, 3), "sum_read_GBps": round(2 * n / read_us / 1e3, 1),
             "copy_us": round(copy_us, 3), "copy_GBps_read_plus_write": round(4 * n / copy_us / 1e3, 1),
             "empty_launch_us": round(empty_us, 3)}
+
+
+def floor_lib():
+    """ctypes handle of the measurement library (streaming-read floor kernel)."""
+    from tree_attention_verify_attn_amd.build import FLOOR_LIB_PATH
+    if not os.path.exists(FLOOR_LIB_PATH):
+        raise RuntimeError(f"{FLOOR_LIB_PATH} is missing: build it with "
+                           "`python -m tree_attention_verify_attn_amd.build`")
+    lib = ctypes.CDLL(FLOOR_LIB_PATH)
+    lib.ta_floor_read.restype = ctypes.c_int
+    lib.ta_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
 
 
 def incache_layout(inp):

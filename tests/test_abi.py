@@ -168,3 +168,39 @@ def test_launch_info_mode_choice():
     with pytest.raises(ta.TreeAttnError):
         ta.launch_info(shape(head_dim=96))
     assert load().tree_attn_launch_info(ctypes.byref(shape()), None) == 1
+
+
+# ---- the measurement library (streaming-read floor kernel)
+FLOOR_HEADER = os.path.join(ROOT, "include", "ta_floor.h")
+
+
+def floor_lib():
+    from tree_attention_verify_attn_amd.build import FLOOR_LIB_PATH
+    lib = ctypes.CDLL(FLOOR_LIB_PATH)
+    lib.ta_floor_read.restype = ctypes.c_int
+    lib.ta_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def test_floor_library_exports_its_header_symbol():
+    names = re.findall(r"\b(ta_floor_\w+)\s*\(", open(FLOOR_HEADER).read())
+    assert names == ["ta_floor_read"]
+    assert hasattr(floor_lib(), "ta_floor_read")
+
+
+@pytest.mark.parametrize("args", [
+    (None, 1024, 8, 256, 4),        # null source
+    (FAKE, 0, 8, 256, 4),           # no bytes
+    (FAKE, 1000, 8, 256, 4),        # not a multiple of 16
+    (FAKE + 8, 1024, 8, 256, 4),    # misaligned source
+    (FAKE, 1024, 0, 256, 4),        # empty grid
+    (FAKE, 1024, 65537, 256, 4),    # grid too large
+    (FAKE, 1024, 8, 96, 4),         # threads not a multiple of 64
+    (FAKE, 1024, 8, 1024, 4),       # threads above 512
+    (FAKE, 1024, 8, 256, 3),        # unsupported loads in flight
+])
+def test_floor_read_rejects_bad_arguments(args):
+    src, nbytes, grid, threads, loads = args
+    assert floor_lib().ta_floor_read(src, nbytes, grid, threads, loads, FAKE, None) == 1
+    assert floor_lib().ta_floor_read(FAKE, 1024, 8, 256, 4, None, None) == 1
