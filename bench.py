@@ -598,6 +598,10 @@ def main() -> int:
     if err != 0:
         raise RuntimeError(f"device error during timing: {ta.status_string(err)}")
 
+    # one call = one attention launch, or two (attention, then combine_kernel)
+    # for a one-sequence shape in the two-launch mode; the roofline is taken
+    # over the whole call either way
+    launch_mode = ta.launch_info(shape)["mode"]
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.config, split) if args.entry == "verify" else None
     mfma_counted, mfma_flops = (measured_mfma(args.config, split) if args.entry == "verify"
@@ -649,11 +653,14 @@ def main() -> int:
             "traffic": traffic,
             "hbm_frac": round(achieved / PEAK_HBM_GBS, 4),
             "kernel": (f"attn_kernel<{'bf16' if inp.dtype == 'bf16' else 'f32'},{D},fused"
-                       + (",tree segments in the ring> " if inp.max_tree_nodes > 64 else "> ")
+                       + (",tree segments in the ring" if inp.max_tree_nodes > 64 else "")
+                       + (",two launches> + combine_kernel " if launch_mode == "two_launch"
+                          else "> ")
                        + ("(tree_attn_verify)" if args.entry == "verify"
                           else "(tree_attn_verify_incache)")
                        if args.entry in ("verify", "incache")
                        else "split path: mask + prefix + suffix + merge kernels"),
+            "launch_mode": launch_mode,
             "mfma_util": round(achieved_tf / peak_tf, 5),
             "mfma_util_counted": mfma_counted,
             "mfma_flops_counted": mfma_flops,

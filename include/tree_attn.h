@@ -338,7 +338,11 @@ int32_t tree_attn_split_tokens(const ta_shape* shape);
  *            1: more items than workgroups: items are handed out by ticket
  *               and the last chunk of each group to arrive combines it alone;
  *            2: decided on the device from the actual prefix lengths (0 when
- *               the items fit the first round, else 1).
+ *               the items fit the first round, else 1);
+ *            3: one sequence, every item in the first round, at least 8
+ *               chunks a group: two launches on the stream, the attention
+ *               kernel storing every chunk's partial and a combine kernel
+ *               folding them (no chunk waits for another).
  * TA_ERR_INVALID_ARG for a null info; shape errors as tree_attn_verify. */
 ta_status tree_attn_launch_info(const ta_shape* shape, int32_t* info);
 

@@ -149,10 +149,21 @@ def test_trees_beyond_256_nodes_refused():
 def test_launch_info_mode_choice():
     """The host's launch plan (no GPU here: sized for a full MI355X, one
     workgroup per CU on 256 CUs)."""
-    # one sequence, 8 KV heads, 8192 tokens: every item in the first round
+    # one sequence, 8 KV heads, 8192 tokens: every item in the first round,
+    # many chunks a group: the partials are combined by a second launch
     i = ta.launch_info(shape())
-    assert i["mode"] == "first_round"
+    assert i["mode"] == "two_launch"
     assert i["max_items"] == 8 * -(-8192 // i["split_tokens"]) and i["max_items"] <= i["grid"] <= 256
+    # the same with 2048-token chunks (4 a group): the chunks meet in the launch
+    i = ta.launch_info(shape(split_tokens=2048))
+    assert i["mode"] == "first_round" and i["max_items"] == 32
+    # trees of more than 64 nodes take two launches too, except bf16 at head
+    # dim 64, whose large-tree kernel has only the one-launch form
+    big = dict(max_tree_nodes=100, total_tree_nodes=100, num_q_heads=8, num_kv_heads=8,
+               max_prefix_len=4096, split_tokens=256)
+    assert ta.launch_info(shape(**big))["mode"] == "two_launch"
+    assert ta.launch_info(shape(**big, head_dim=64, dtype=ta.DTYPE_F32))["mode"] == "two_launch"
+    assert ta.launch_info(shape(**big, head_dim=64))["mode"] == "first_round"
     # one sequence forced into small chunks: at most 64 chunks a group (64 tokens
     # become 128), 8 * 64 items handed out by ticket
     i = ta.launch_info(shape(split_tokens=64))

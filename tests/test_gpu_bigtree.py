@@ -159,6 +159,27 @@ def test_fused_verify_large_tree_one_sequence_split_chunks():
     assert_close_lse(host(lse), l_want, 1e-3, "one-sequence big-tree lse")
 
 
+@pytest.mark.parametrize("dtype,D,mode", [("bf16", 128, "two_launch"), ("f32", 64, "two_launch"),
+                                          ("bf16", 64, "first_round")])
+def test_fused_verify_large_tree_one_sequence_first_round(dtype, D, mode):
+    # one sequence, a 256-node tree, 16 chunks a group and every item in the
+    # first round: two launches (partials, then the combine kernel), except
+    # bf16 at head dim 64, whose large-tree kernel meets in the launch
+    import tree_attention_verify_attn_amd as ta
+    rng = np.random.default_rng(97)
+    inp = _big(97, [random_tree(rng, 256)], [4000], Hq=2, Hkv=2, dtype=dtype, D=D)
+    d = to_device(inp, max_tree_nodes=256, split_tokens=256)
+    info = ta.launch_info(d.shape)
+    say(f"fused verify, one sequence, 256-node tree, {dtype} D={D}: {info}")
+    assert info["mode"] == mode, info
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(out), o_want, tol_o, f"one-sequence big-tree {dtype} D={D} o")
+    assert_close_lse(host(lse), l_want, tol_l, f"one-sequence big-tree {dtype} D={D} lse")
+
+
 def test_fused_verify_draft_side_matches_split():
     # the draft-side shape through the fused verify, against the oracle and
     # the split path

@@ -38,9 +38,13 @@ class _ForceLeave:
 
 
 LEAVE_CASES = [
-    ("cfg2", lambda: make_config(2), 0),                       # one sequence, 26 chunks a group
+    # one sequence with 4 chunks a group meets in the launch (with 8 or more,
+    # as the library's own chunk gives the 8k verify, it takes two launches
+    # and has no meeting: the forced leave must then change nothing)
+    ("cfg2-split2048", lambda: make_config(2), 2048),          # one sequence, 4 chunks a group
+    ("cfg4-split2048", lambda: make_config(4), 2048),          # one group of 4 chunks
+    ("cfg2", lambda: make_config(2), 0),                       # two launches, 26 chunks a group
     ("cfg3", lambda: make_config(3), 0),                       # 32 sequences, device-chosen chunk
-    ("cfg4-split128", lambda: make_config(4), 128),            # one group of 64 chunks
     ("d64-f32", lambda: small_inputs(120, dtype="f32", B=2, Hq=4, Hkv=2, D=64,
                                      prefix_lens=(2000, 700)), 128),
 ]

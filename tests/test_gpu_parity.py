@@ -187,7 +187,59 @@ def test_verify_ticket_many_chunks(name, make, split):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("split", [64, 128, 256, 1024, 4096])
+def _one_seq(seed, *, dtype, Hq, Hkv, D, P, tree=None, extra_cols=0):
+    rng = np.random.default_rng(seed)
+    return make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       prefix_lens=[P], trees=[tree or TREE_12], rng=rng, seed=seed,
+                       name=f"one-seq{seed}", permute_blocks=True, spare_blocks=3,
+                       extra_table_cols=extra_cols)
+
+
+# One sequence whose groups have at least 8 chunks, all in the first round:
+# the attention kernel stores every chunk's partial and a second launch
+# (combine_kernel) folds them.  One case per combine instantiation (output
+# type, head dim), the largest chunk count at each head dim, a tree of more
+# than 64 nodes (the large-tree attention kernel, several row passes), and a
+# prefix far shorter than max_prefix_len (chunks with no key at all).
+TWO_LAUNCH_CASES = [
+    ("bf16-d64-s12", lambda: _one_seq(500, dtype="bf16", Hq=8, Hkv=2, D=64, P=3000), 256, None),
+    ("f32-d128-s40", lambda: _one_seq(501, dtype="f32", Hq=4, Hkv=1, D=128, P=5000), 128, None),
+    ("f32-d64-s64", lambda: _one_seq(502, dtype="f32", Hq=6, Hkv=2, D=64, P=4096), 64, None),
+    ("bf16-d128-s64", lambda: _one_seq(503, dtype="bf16", Hq=5, Hkv=1, D=128, P=8100), 128, None),
+    ("bf16-200-node-tree", lambda: _one_seq(504, dtype="bf16", Hq=2, Hkv=1, D=128, P=2048,
+                                            tree=[-1] + [i // 2 for i in range(199)]), 256, None),
+    ("empty-chunks", lambda: _one_seq(505, dtype="bf16", Hq=8, Hkv=2, D=128, P=900,
+                                      extra_cols=60), 256, 4096),
+]
+
+
+@pytest.mark.parametrize("name,make,split,max_p", TWO_LAUNCH_CASES,
+                         ids=[c[0] for c in TWO_LAUNCH_CASES])
+def test_verify_two_launch(name, make, split, max_p):
+    import tree_attention_verify_attn_amd as ta
+    inp = make()
+    d = to_device(inp, split_tokens=split, max_prefix_len=max_p)
+    info = ta.launch_info(d.shape)
+    say(f"two-launch verify {name}: {info}")
+    assert info["mode"] == "two_launch", info
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, f"two-launch {name}")
+    # the prefix pass alone takes the same two launches (fp32 output)
+    po, pl = ta.prefix(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
+                       d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    wpo, wpl = oracle.prefix_only(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(po), wpo, tol_o, f"two-launch {name} prefix o")
+    assert_close_lse(host(pl), wpl, tol_l, f"two-launch {name} prefix lse")
+    # and again on the same workspace: nothing to reset, the same result
+    out2, lse2 = run_verify(d)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("split", [64, 128, 256, 1024, 2048, 4096])
 def test_verify_split_sizes(split):
     inp = make_config(4)
     d = to_device(inp, split_tokens=split)

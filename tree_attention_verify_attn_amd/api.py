@@ -86,7 +86,7 @@ def launch_info(shape: Shape) -> dict:
     info = (ctypes.c_int32 * 4)()
     _check(load().tree_attn_launch_info(ctypes.byref(shape), info), "tree_attn_launch_info")
     return {"split_tokens": info[0], "grid": info[1], "max_items": info[2],
-            "mode": ("first_round", "ticket", "device")[info[3]]}
+            "mode": ("first_round", "ticket", "device", "two_launch")[info[3]]}
 
 
 def alloc_workspace(shape: Shape, device="cuda", min_bytes: int = 256) -> torch.Tensor:

@@ -289,11 +289,26 @@ int launch_status() {
 // keeps its registers.
 bool big_fused(const ta_shape* s, bool fused) { return fused && s->max_tree_nodes > kMaxTree; }
 
+// Instantiations that have the two-launch form.  The compiler's gfx950
+// backend rejects the bf16, D = 64 large-tree attention kernel in that form
+// (an illegal VOPC compare on src_shared_base), so that one combination meets
+// in the launch whatever its chunk count.
+template <typename T, int D, bool BIG>
+constexpr bool two_launch_builds() { return !(sizeof(T) == 2 && D == 64 && BIG); }
+bool two_launch_builds(const ta_shape* s, bool fused) {
+  return !(s->dtype == TA_DTYPE_BF16 && s->head_dim == 64 && big_fused(s, fused));
+}
+
 template <typename T, int D, bool FUSED>
-const void* attn_ptr(bool big) {
+const void* attn_ptr(bool big, bool two = false) {
   if constexpr (FUSED)
-    if (big) return reinterpret_cast<const void*>(&attn_kernel<T, D, true, true>);
-  return reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED>);
+    if (big) {
+      if constexpr (two_launch_builds<T, D, true>())
+        if (two) return reinterpret_cast<const void*>(&attn_kernel<T, D, true, true, true>);
+      return reinterpret_cast<const void*>(&attn_kernel<T, D, true, true>);
+    }
+  return two ? reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED, false, true>)
+             : reinterpret_cast<const void*>(&attn_kernel<T, D, FUSED>);
 }
 
 const void* attn_kernel_ptr(const ta_shape* s, bool fused) {
@@ -321,6 +336,26 @@ int launch_suffix(const ta_shape* s, Params p, unsigned grid, hipStream_t stream
   const size_t dyn = size_t(ns) * slot;
   if (ensure_dyn_lds(kern, dyn) != kOk) return kErrHip;
   hipLaunchKernelGGL((suffix_kernel<T, D>), dim3(grid), dim3(kAttnThreads), dyn, stream, p);
+  return launch_status();
+}
+
+// The second launch of a two-launch call (after attn_kernel on the same
+// stream): QG row slots per row, the fewest whose QMAX partial loads per lane
+// cover the S chunks; wpg workgroups per group.
+template <typename T, int D, bool FUSED>
+int launch_combine(const Params& p, hipStream_t stream) {
+  const int st = launch_status();
+  if (st != kOk) return st;
+  constexpr int NSLOT = kAttnThreads / (D / 4);
+  constexpr int QMAX = kMaxSplits / NSLOT;
+  int qg = 1;
+  while (qg * QMAX < p.s_max) qg <<= 1;
+  const int rows = p.total_nodes * p.group;
+  const int rp = cdiv(rows, kRowsPerPass);
+  const int wpg = cdiv(rows < kRowsPerPass ? rows : kRowsPerPass, NSLOT / qg);
+  using OutT = typename std::conditional<FUSED, T, float>::type;
+  hipLaunchKernelGGL((combine_kernel<OutT, D>), dim3(unsigned(p.hkv * rp * wpg)),
+                     dim3(kAttnThreads), 0, stream, p, wpg, qg);
   return launch_status();
 }
 
@@ -354,6 +389,26 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
   //    8k verify, though every exchange still goes through device-coherent
   //    memory.
   p.xcd_major = p.single && p.single_items % 8 == 0 && p.single_items <= first ? 1 : 0;
+  // Two launches for a one-sequence launch whose groups have many chunks, all
+  // in the first round: attn_kernel ends at the partial stores and
+  // combine_kernel, queued behind it, folds them.  The kernel boundary costs
+  // less than the meeting of many chunks in the launch (measured on the 8k
+  // verify: 17.3 us against 17.8 with 26 chunks a group, 13.5 against 14.9
+  // with 64), and more where a group has only a few.
+  const bool two = p.single && p.single_items <= first && p.s_max >= kTwoLaunchMinChunks &&
+                   two_launch_builds(s, FUSED);
+  if (two) {
+    if (ensure_dyn_lds(attn_ptr<T, D, FUSED>(big, true), dyn) != kOk) return kErrHip;
+    if constexpr (FUSED && two_launch_builds<T, D, true>())
+      if (big) {
+        hipLaunchKernelGGL((attn_kernel<T, D, true, true, true>), dim3(unsigned(first)),
+                           dim3(kAttnThreads), dyn, stream, p);
+        return launch_combine<T, D, FUSED>(p, stream);
+      }
+    hipLaunchKernelGGL((attn_kernel<T, D, FUSED, false, true>), dim3(unsigned(first)),
+                       dim3(kAttnThreads), dyn, stream, p);
+    return launch_combine<T, D, FUSED>(p, stream);
+  }
   if constexpr (FUSED)
     if (big) {
       hipLaunchKernelGGL((attn_kernel<T, D, true, true>), dim3(unsigned(first)), dim3(kAttnThreads),
@@ -444,8 +499,9 @@ ta_status tree_attn_launch_info(const ta_shape* shape, int32_t* info) {
   int grid = L.item_slots < cap ? L.item_slots : cap;
   if (grid < 1) grid = 1;
   int mode;
-  if (one_sequence(shape))
-    mode = L.item_slots <= grid ? 0 : 1;  // items numbered statically: the count is known here
+  if (one_sequence(shape))  // items numbered statically: the count is known here
+    mode = L.item_slots > grid ? 1
+           : L.s_max >= kTwoLaunchMinChunks && two_launch_builds(shape, true) ? 3 : 0;
   else if (chunk_auto(shape))
     mode = L.num_groups > grid ? 1 : 2;   // the kernel fits every item in the first round if it can
   else

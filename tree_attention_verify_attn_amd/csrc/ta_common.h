@@ -17,6 +17,9 @@ constexpr int kMaxTreeSplit = 256; // split path: up to four mask words per tree
 constexpr int kMaxBatch = 2048;   // per-workgroup item table lives in LDS
 constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
+// One-sequence launches whose groups have at least this many chunks end the
+// attention kernel at the partial stores and combine in a second launch.
+constexpr int kTwoLaunchMinChunks = 8;
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 constexpr int kMaxRingSlots = 2;       // KV blocks the attention kernel keeps in LDS

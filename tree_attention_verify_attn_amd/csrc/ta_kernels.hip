@@ -13,6 +13,8 @@
 //   mask_kernel      ancestor-or-self mask words of every tree (one wave per tree)
 //   attn_kernel      prefix pass; with FUSED it also builds the tree mask, runs
 //                    the tree piece and merges (the fused verify)
+//   combine_kernel   the split reduce of a one-sequence launch in two launches:
+//                    folds the chunk partials of every group into its rows
 //   suffix_kernel    tree piece on its own (split path), on the same MFMA path
 //   merge_kernel     merge of two (o, lse) results (split path)
 //
@@ -36,6 +38,9 @@
 //     device-coherent stores, the chunks meet at a sense-reversing barrier and
 //     split the final combine: each takes some rows, folds every chunk partial
 //     with its log-sum-exp weight and writes the output rows.
+//     A one-sequence launch whose groups have many chunks (the 8k-context
+//     verify) instead ends at the partial stores; combine_kernel, queued right
+//     after it on the same stream, does the combine.
 #include <type_traits>
 
 #include "ta_device.h"
@@ -620,7 +625,7 @@ constexpr float kRescaleSlack = 8.f;
 // SUFFIX: the tree piece of the split path on its own -- no prefix, the tree
 // keys streamed through the ring in segments of 64 nodes, each under its
 // word of the precomputed ancestor-or-self mask (p.mask_in), fp32 outputs.
-template <typename T, int D, bool FUSED, bool SUFFIX = false, bool BIG = false>
+template <typename T, int D, bool FUSED, bool SUFFIX = false, bool BIG = false, bool TWO = false>
 __device__ __forceinline__ void process_item(const Params& p, unsigned char* ring,
                                              unsigned char* tree_lds,
                                              SmemMisc& sm, const Item& it, int slot_index,
@@ -764,7 +769,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // partials are written.  Each counts itself as started here, once its
   // chunk is known to be non-empty and before its first KV transfer, so
   // that the meeting can tell whether every chunk of the group is running.
-  const bool meet = !SUFFIX && !solo_combine && S > 1;
+  const bool meet = !SUFFIX && !solo_combine && S > 1 && !TWO;
   if (meet && tid == 0) __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // trees of more than 64 nodes (fused): their 64-node segments follow the
   // chunk's KV blocks through the ring, under mask words built in LDS
@@ -1327,6 +1332,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     }
   }
 
+  // two launches: combine_kernel, next on the stream, folds the partials
+  if constexpr (TWO) return;
+
   // ---- meet the other chunks of the group.  The arrival counter goes from 0
   // to S, and the chunk that brings it to S resets it to 0 (ready for the next
   // call).  Every chunk's partial stores are complete before its arrival, so
@@ -1545,7 +1553,9 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   }
 }
 
-template <typename T, int D, bool FUSED, bool BIG = false>
+// TWO: a one-sequence launch in two launches (see combine_kernel); the
+// chunks end at their partial stores.
+template <typename T, int D, bool FUSED, bool BIG = false, bool TWO = false>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   using Gm = Geo<T, D>;
   // dynamic LDS: the KV ring (ns slots), the tree rows (K then V), the table
@@ -1578,7 +1588,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
   const bool tickets = items > p.first_round;  // else the first round covers every item
   while (li < items) {
     const Item it = p.single ? decode_single(p, li) : decode_item(p, chunk, cum, ot, pl, perm, li);
-    process_item<T, D, FUSED, false, BIG>(p, ring, tree_lds, sm, it, li, tickets);
+    process_item<T, D, FUSED, false, BIG, TWO>(p, ring, tree_lds, sm, it, li, tickets);
     if (!tickets) break;
     __syncthreads();
     if (tid == 0) sm.bcast[0] = p.first_round + int(atomicAdd(&p.hdr->ticket, 1u));
@@ -1597,6 +1607,125 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
       __hip_atomic_store(&p.hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// ========================================================= combine kernel
+// The split reduce of a one-sequence launch made in two launches: attn_kernel
+// has stored every chunk's partial (unnormalised o rows, running max m and
+// running sum l, base 2) in the chunk's slot, and this kernel folds them.
+// [merge_attentions over disjoint KV chunks: pith.science verdict record,
+// pith_extraction.supporting_citations (Juravsky et al. 2024)]
+// For a row with partials (o_c, m_c, l_c), c < S:
+//   M = max_c m_c,  w_c = 2^(m_c - M),  o = sum_c w_c o_c / sum_c w_c l_c,
+//   lse = (M + log2 sum_c w_c l_c) ln 2  (o = 0, lse = -inf when M = -inf).
+// Items are numbered as in attn_kernel's one-sequence launches: group
+// t = g * RP + rp (KV head g, row pass rp) owns the slots t * S .. t * S + S - 1.
+// Workgroup w takes rows_per_wg = NSLOT / QG rows of group w / wpg: D / 4
+// lanes (a row slot) cover one row's head dim, 4 elements each, and QG row
+// slots split its S partials between them, QMAX loads per lane, all issued
+// up front; the QG slots then meet in LDS.  OutT: the output element type
+// (the shape's dtype for the fused verify, fp32 for the prefix pass).
+template <typename OutT, int D>
+__global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg, int QG) {
+  constexpr int L4 = D / 4;
+  constexpr int NSLOT = kAttnThreads / L4;
+  constexpr int QMAX = kMaxSplits / NSLOT;  // QG * QMAX >= S for S <= kMaxSplits
+  __shared__ float red_m[NSLOT];
+  __shared__ float red_l[NSLOT];
+  __shared__ __attribute__((aligned(16))) float red_o[NSLOT * D];
+  const int tid = threadIdx.x;
+  const int S = p.s_max;
+  const int G = p.group;
+  const int R = p.total_nodes * G;
+  const int RP = cdiv(R, kRowsPerPass);
+  const int t = int(blockIdx.x) / wpg;
+  const int rp = t % RP;
+  const int g = t / RP;
+  const int rlo = rp * kRowsPerPass;
+  const int rcount = min(kRowsPerPass, R - rlo);
+  const int rs = tid / L4;  // row slot
+  const int d4 = tid % L4;
+  const int qg = rs % QG;
+  const int rb = rs / QG;
+  const int r = (int(blockIdx.x) % wpg) * (NSLOT / QG) + rb;
+  const bool valid = r < rcount;
+  const float* g0 = p.partials + size_t(t) * size_t(S) * p.slot_floats;  // chunk 0's slot
+  const uint32_t gbytes = uint32_t(S) * uint32_t(p.slot_floats) * 4u;
+  const int moff = p.rows_slot * D;
+  const int loff = moff + p.rows_slot;
+  float mq[QMAX], lq[QMAX];
+  float4 oq[QMAX];
+#pragma unroll
+  for (int j = 0; j < QMAX; ++j) {
+    const int q = qg + QG * j;
+    if (valid && q < S) {
+      const uint32_t so = uint32_t(q * p.slot_floats);
+      mq[j] = coherent_load4(g0, gbytes, (so + moff + r) * 4u);
+      lq[j] = coherent_load4(g0, gbytes, (so + loff + r) * 4u);
+      oq[j] = coherent_load16(g0, gbytes, (so + r * D + 4 * d4) * 4u);
+    } else {
+      mq[j] = -INFINITY;
+      lq[j] = 0.f;
+      oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < QMAX; ++j) mloc = fmaxf(mloc, mq[j]);
+  if (d4 == 0) red_m[rs] = mloc;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int x = 0; x < QG; ++x) M = fmaxf(M, red_m[rb * QG + x]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < QMAX; ++j) {
+      const float wq = exp2_fast(mq[j] - M);
+      L = fmaf(wq, lq[j], L);
+      acc.x = fmaf(wq, oq[j].x, acc.x);
+      acc.y = fmaf(wq, oq[j].y, acc.y);
+      acc.z = fmaf(wq, oq[j].z, acc.z);
+      acc.w = fmaf(wq, oq[j].w, acc.w);
+    }
+  }
+  *reinterpret_cast<float4*>(red_o + rs * D + 4 * d4) = acc;
+  if (d4 == 0) red_l[rs] = L;
+  __syncthreads();
+  if (qg != 0 || !valid) return;
+  float Lt = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int x = 0; x < QG; ++x) {
+    const int sx = rb * QG + x;
+    Lt += red_l[sx];
+    const float4 ox = *reinterpret_cast<const float4*>(red_o + sx * D + 4 * d4);
+    o.x += ox.x;
+    o.y += ox.y;
+    o.z += ox.z;
+    o.w += ox.w;
+  }
+  float lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float inv = 1.f / Lt;
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
+    lse = (M + __log2f(Lt)) * kLn2;
+  } else {
+    o = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int rr = rlo + r;
+  const size_t orow = size_t(rr / G) * p.hq + g * G + rr % G;
+  OutT* dst = static_cast<OutT*>(p.out) + orow * D + 4 * d4;
+  if constexpr (sizeof(OutT) == 2) {
+    const uint32_t lo = uint32_t(f32_to_bf16(o.x)) | (uint32_t(f32_to_bf16(o.y)) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(o.z)) | (uint32_t(f32_to_bf16(o.w)) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(dst) = o;
+  }
+  if (d4 == 0 && p.lse_out) p.lse_out[orow] = lse;
 }
 
 // ============================================================ mask kernel
