@@ -105,8 +105,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(config_index: int, split: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources and the same workload; else None."""
+    """HBM bytes per call (both launches of a two-launch call) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources and
+    the same workload; else None."""
     path = TRAFFIC_FILES.get(config_index)
     if path is None:
         return None
@@ -119,7 +120,7 @@ def measured_traffic(config_index: int, split: int):
         return None
     if rec.get("config") != config_index or rec.get("split_tokens") != split:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
 
 
 def measured_mfma(config_index: int, split: int):
@@ -183,7 +184,6 @@ def summarize_trace(path: str, kernel: str) -> dict:
     """Per-dispatch duration statistics of the kernels whose name contains
     `kernel`, from a rocprofv3 --kernel-trace CSV (kernel_trace.csv)."""
     import csv
-    import statistics
     durs = []
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
@@ -191,8 +191,27 @@ def summarize_trace(path: str, kernel: str) -> dict:
                 durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
     if not durs:
         raise SystemExit(f"no dispatch of a kernel matching {kernel!r} in {path}")
+    out = {"kernel": kernel, **_dist(durs)}
+    # a call made in two launches: each attention dispatch followed by a
+    # combine_kernel dispatch on the same queue; per call, the span from the
+    # first's start to the second's end (the gap between them included)
+    with open(path, newline="") as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    spans, comb = [], []
+    for a, b in zip(rows, rows[1:]):
+        if kernel in a.get("Kernel_Name", "") and "combine_kernel" in b.get("Kernel_Name", ""):
+            spans.append((int(b["End_Timestamp"]) - int(a["Start_Timestamp"])) / 1e3)
+            comb.append((int(b["End_Timestamp"]) - int(b["Start_Timestamp"])) / 1e3)
+    if spans:
+        out["combine_kernel"] = _dist(comb)
+        out["call_span"] = _dist(spans)
+    return out
+
+
+def _dist(durs) -> dict:
+    import statistics
     q = statistics.quantiles(durs, n=10, method="inclusive")
-    return {"kernel": kernel, "dispatches": len(durs), "mean_us": round(statistics.fmean(durs), 3),
+    return {"dispatches": len(durs), "mean_us": round(statistics.fmean(durs), 3),
             "p10_us": round(q[0], 3), "median_us": round(statistics.median(durs), 3),
             "p90_us": round(q[8], 3), "min_us": round(min(durs), 3), "max_us": round(max(durs), 3)}
 

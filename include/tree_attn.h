@@ -182,7 +182,11 @@ ta_status tree_attn_merge(int64_t rows, int32_t head_dim, ta_dtype out_dtype,
                           hipStream_t stream);
 
 /* Fused verify: prefix pass + mask build + suffix pass + merge in one kernel
- * launch.  Writes out (shape->dtype) and lse_out (fp32, may be NULL).  Trees
+ * launch; for one sequence whose (KV head, row pass) groups have several
+ * prefix chunks, all running at once (the 8k-context verify), in two launches
+ * on `stream`: the attention kernel storing every chunk's partial result in
+ * the workspace, then a combine kernel merging them (tree_attn_launch_info
+ * mode 3).  Writes out (shape->dtype) and lse_out (fp32, may be NULL).  Trees
  * of up to 256 nodes (max_tree_nodes <= 256, else TA_ERR_UNSUPPORTED).  Up to
  * 64 nodes the tree rows sit in LDS beside the KV ring; larger trees stream
  * through the ring in 64-node segments after the last chunk's KV blocks,
@@ -339,8 +343,8 @@ int32_t tree_attn_split_tokens(const ta_shape* shape);
  *               and the last chunk of each group to arrive combines it alone;
  *            2: decided on the device from the actual prefix lengths (0 when
  *               the items fit the first round, else 1);
- *            3: one sequence, every item in the first round, at least 8
- *               chunks a group: two launches on the stream, the attention
+ *            3: one sequence, every item in the first round, more than one
+ *               chunk a group: two launches on the stream, the attention
  *               kernel storing every chunk's partial and a combine kernel
  *               folding them (no chunk waits for another).
  * TA_ERR_INVALID_ARG for a null info; shape errors as tree_attn_verify. */

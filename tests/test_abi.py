@@ -154,9 +154,12 @@ def test_launch_info_mode_choice():
     i = ta.launch_info(shape())
     assert i["mode"] == "two_launch"
     assert i["max_items"] == 8 * -(-8192 // i["split_tokens"]) and i["max_items"] <= i["grid"] <= 256
-    # the same with 2048-token chunks (4 a group): the chunks meet in the launch
+    # the same with 2048-token chunks (4 a group): two launches as well; with
+    # one chunk a group the attention kernel writes the output rows itself
     i = ta.launch_info(shape(split_tokens=2048))
-    assert i["mode"] == "first_round" and i["max_items"] == 32
+    assert i["mode"] == "two_launch" and i["max_items"] == 32
+    i = ta.launch_info(shape(split_tokens=4096, max_prefix_len=4096))
+    assert i["mode"] == "first_round" and i["max_items"] == 8
     # trees of more than 64 nodes take two launches too, except bf16 at head
     # dim 64, whose large-tree kernel has only the one-launch form
     big = dict(max_tree_nodes=100, total_tree_nodes=100, num_q_heads=8, num_kv_heads=8,

@@ -17,7 +17,7 @@ import torch
 import oracle
 from gpu_util import assert_close, assert_close_lse, host, run_verify, say, to_device, tolerances
 from helpers import small_inputs
-from workloads import TREE_12, make_config
+from workloads import TREE_12, make_config, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +38,12 @@ class _ForceLeave:
 
 
 LEAVE_CASES = [
-    # one sequence with 4 chunks a group meets in the launch (with 8 or more,
-    # as the library's own chunk gives the 8k verify, it takes two launches
-    # and has no meeting: the forced leave must then change nothing)
-    ("cfg2-split2048", lambda: make_config(2), 2048),          # one sequence, 4 chunks a group
-    ("cfg4-split2048", lambda: make_config(4), 2048),          # one group of 4 chunks
+    # one sequence: bf16 at head dim 64 with a tree of more than 64 nodes is
+    # the one-sequence shape that still meets in the launch (others take two
+    # launches and have no meeting: the forced leave must change nothing)
+    ("one-seq-d64-big", lambda: make_inputs(
+        dtype="bf16", num_q_heads=2, num_kv_heads=2, head_dim=64, prefix_lens=[3000],
+        trees=[[-1] + [i // 3 for i in range(99)]], rng=np.random.default_rng(60), seed=60), 256),
     ("cfg2", lambda: make_config(2), 0),                       # two launches, 26 chunks a group
     ("cfg3", lambda: make_config(3), 0),                       # 32 sequences, device-chosen chunk
     ("d64-f32", lambda: small_inputs(120, dtype="f32", B=2, Hq=4, Hkv=2, D=64,

@@ -195,14 +195,16 @@ def _one_seq(seed, *, dtype, Hq, Hkv, D, P, tree=None, extra_cols=0):
                        extra_table_cols=extra_cols)
 
 
-# One sequence whose groups have at least 8 chunks, all in the first round:
-# the attention kernel stores every chunk's partial and a second launch
+# One sequence whose groups have several chunks, all in the first round: the
+# attention kernel stores every chunk's partial and a second launch
 # (combine_kernel) folds them.  One case per combine instantiation (output
-# type, head dim), the largest chunk count at each head dim, a tree of more
-# than 64 nodes (the large-tree attention kernel, several row passes), and a
-# prefix far shorter than max_prefix_len (chunks with no key at all).
+# type, head dim), the largest chunk count at each head dim, two chunks, a
+# tree of more than 64 nodes (the large-tree attention kernel, several row
+# passes), and a prefix far shorter than max_prefix_len (chunks with no key
+# at all).
 TWO_LAUNCH_CASES = [
     ("bf16-d64-s12", lambda: _one_seq(500, dtype="bf16", Hq=8, Hkv=2, D=64, P=3000), 256, None),
+    ("bf16-d128-s2", lambda: _one_seq(506, dtype="bf16", Hq=8, Hkv=2, D=128, P=1500), 1024, None),
     ("f32-d128-s40", lambda: _one_seq(501, dtype="f32", Hq=4, Hkv=1, D=128, P=5000), 128, None),
     ("f32-d64-s64", lambda: _one_seq(502, dtype="f32", Hq=6, Hkv=2, D=64, P=4096), 64, None),
     ("bf16-d128-s64", lambda: _one_seq(503, dtype="bf16", Hq=5, Hkv=1, D=128, P=8100), 128, None),

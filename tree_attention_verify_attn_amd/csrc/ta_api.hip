@@ -389,12 +389,13 @@ int launch_attn(const ta_shape* s, Params p, const WsLayout& L, hipStream_t stre
   //    8k verify, though every exchange still goes through device-coherent
   //    memory.
   p.xcd_major = p.single && p.single_items % 8 == 0 && p.single_items <= first ? 1 : 0;
-  // Two launches for a one-sequence launch whose groups have many chunks, all
-  // in the first round: attn_kernel ends at the partial stores and
+  // Two launches for a one-sequence launch whose groups have several chunks,
+  // all in the first round: attn_kernel ends at the partial stores and
   // combine_kernel, queued behind it, folds them.  The kernel boundary costs
-  // less than the meeting of many chunks in the launch (measured on the 8k
-  // verify: 17.3 us against 17.8 with 26 chunks a group, 13.5 against 14.9
-  // with 64), and more where a group has only a few.
+  // less than the chunks' meeting in the launch, and the attention kernel
+  // without the meeting and combine code is leaner (measured on the 8k
+  // verify: 16.2 us against 17.5 with 26 chunks a group, 12.6 against 14.8
+  // with 64, 61.2 against 63.2 with 2).
   const bool two = p.single && p.single_items <= first && p.s_max >= kTwoLaunchMinChunks &&
                    two_launch_builds(s, FUSED);
   if (two) {

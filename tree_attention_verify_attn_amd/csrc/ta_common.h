@@ -19,7 +19,7 @@ constexpr int kRowsPerPass = 64;  // grouped query rows one work item covers
 constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row pass)
 // One-sequence launches whose groups have at least this many chunks end the
 // attention kernel at the partial stores and combine in a second launch.
-constexpr int kTwoLaunchMinChunks = 8;
+constexpr int kTwoLaunchMinChunks = 2;
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 constexpr int kMaxRingSlots = 2;       // KV blocks the attention kernel keeps in LDS

@@ -38,7 +38,7 @@
 //     device-coherent stores, the chunks meet at a sense-reversing barrier and
 //     split the final combine: each takes some rows, folds every chunk partial
 //     with its log-sum-exp weight and writes the output rows.
-//     A one-sequence launch whose groups have many chunks (the 8k-context
+//     A one-sequence launch whose groups have several chunks (the 8k-context
 //     verify) instead ends at the partial stores; combine_kernel, queued right
 //     after it on the same stream, does the combine.
 #include <type_traits>
