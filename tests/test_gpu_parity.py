@@ -241,6 +241,34 @@ def test_verify_two_launch(name, make, split, max_p):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def test_verify_two_launch_prefix_shorter_than_before():
+    """One workspace, one shape (max_prefix_len 4096, 16 chunks a group), the
+    actual prefix length shrinking from call to call: the chunks past it store
+    nothing, so the combine must not fold what earlier calls left in their
+    slots; with one chunk left the attention kernel writes the rows itself and
+    the combine must leave them; with none, every row is the tree alone."""
+    import dataclasses
+
+    import tree_attention_verify_attn_amd as ta
+    base = _one_seq(507, dtype="bf16", Hq=8, Hkv=2, D=128, P=4000)
+    d = to_device(base, split_tokens=256)
+    assert ta.launch_info(d.shape)["mode"] == "two_launch"
+    for P in (4000, 900, 4000, 200, 0, 3100):
+        say(f"two-launch verify, prefix {P} of at most 4000")
+        inp = dataclasses.replace(base, prefix_lens=np.array([P], dtype=np.int32))
+        d.prefix_lens.fill_(P)
+        out, lse = run_verify(d)
+        assert ta.get_error(d.workspace) == 0
+        _check_verify(inp, out, lse, f"two-launch prefix {P}")
+        po, pl = ta.prefix(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
+                           d.tree_offsets, d.workspace)
+        torch.cuda.synchronize()
+        wpo, wpl = oracle.prefix_only(inp)
+        tol_o, tol_l = tolerances(inp)
+        assert_close(host(po), wpo, tol_o, f"two-launch prefix pass {P} o")
+        assert_close_lse(host(pl), wpl, tol_l, f"two-launch prefix pass {P} lse")
+
+
 @pytest.mark.parametrize("split", [64, 128, 256, 1024, 2048, 4096])
 def test_verify_split_sizes(split):
     inp = make_config(4)

@@ -684,7 +684,7 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
   // previous item lands here, not between the loads of this trip
   wait_vm<0>();
   // hidden (sm.hid): a compiler wait for it would stall the loads below
-  if constexpr (!SUFFIX)
+  if constexpr (!SUFFIX && !TWO)
     if (tid == 0) hidden_load<true>(reinterpret_cast<const int*>(sense), &sm.hid[kHidSense]);
   uint4 qv[QCH];
   {
@@ -1619,7 +1619,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
 //   M = max_c m_c,  w_c = 2^(m_c - M),  o = sum_c w_c o_c / sum_c w_c l_c,
 //   lse = (M + log2 sum_c w_c l_c) ln 2  (o = 0, lse = -inf when M = -inf).
 // Items are numbered as in attn_kernel's one-sequence launches: group
-// t = g * RP + rp (KV head g, row pass rp) owns the slots t * S .. t * S + S - 1.
+// t = g * RP + rp (KV head g, row pass rp) owns the slots t * S .. t * S + S - 1,
+// of which the first cdiv(P, chunk) ran (P the actual prefix length).
 // Workgroup w takes rows_per_wg = NSLOT / QG rows of group w / wpg: D / 4
 // lanes (a row slot) cover one row's head dim, 4 elements each, and QG row
 // slots split its S partials between them, QMAX loads per lane, all issued
@@ -1653,6 +1654,11 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
   const uint32_t gbytes = uint32_t(S) * uint32_t(p.slot_floats) * 4u;
   const int moff = p.rows_slot * D;
   const int loff = moff + p.rows_slot;
+  // The grid was sized from max_prefix_len; the actual prefix length, read in
+  // the same trip as the partials, says which chunks ran: chunks past it
+  // stored nothing this call (their slots hold older data), and with a single
+  // chunk the attention kernel wrote the output rows itself.
+  const int p_read = p.prefix_lens[0];
   float mq[QMAX], lq[QMAX];
   float4 oq[QMAX];
 #pragma unroll
@@ -1669,9 +1675,19 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
       oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  const int P = p_read >= 0 && p_read <= p.max_prefix ? p_read : 0;  // as attn_kernel reads it
+  const int s_run = P > 0 ? cdiv(P, p.chunk) : 1;
+#pragma unroll
+  for (int j = 0; j < QMAX; ++j)
+    if (qg + QG * j >= s_run) {
+      mq[j] = -INFINITY;
+      lq[j] = 0.f;
+      oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   float mloc = -INFINITY;
 #pragma unroll
   for (int j = 0; j < QMAX; ++j) mloc = fmaxf(mloc, mq[j]);
+  if (s_run == 1) return;  // the same in every thread
   if (d4 == 0) red_m[rs] = mloc;
   __syncthreads();
   float M = -INFINITY;
