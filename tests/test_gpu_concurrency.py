@@ -134,24 +134,32 @@ def _copy_inputs(dst, src):
         getattr(dst, name).copy_(getattr(src, name))
 
 
+def _one_seq_inputs(seed):
+    # one sequence, 12 chunks a group: two launches (attention, then combine)
+    return small_inputs(seed, dtype="bf16", B=1, Hq=8, Hkv=2, D=128, prefix_lens=(3000,),
+                        trees=[TREE_12])
+
+
 def test_verify_graph_capture_replay():
-    """workspace_init and three verify calls (first-round, ticket mode, and
-    first-round again, on one workspace) captured in a HIP graph and replayed
-    with new inputs: every replay matches the oracle for its inputs, also
-    with eager work between replays."""
+    """workspace_init and four verify calls (first-round, ticket mode, first-
+    round again, and a one-sequence call in two launches, on one workspace)
+    captured in a HIP graph and replayed with new inputs: every replay matches
+    the oracle for its inputs, also with eager work between replays."""
     import tree_attention_verify_attn_amd as ta
-    a0, t0 = _same_shape_inputs(200), _ticket_inputs(210)
-    da, dt = to_device(a0), to_device(t0, split_tokens=128)
-    ws = torch.zeros(max(ta.workspace_size(da.shape), ta.workspace_size(dt.shape)),
+    a0, t0, s0 = _same_shape_inputs(200), _ticket_inputs(210), _one_seq_inputs(220)
+    da, dt, ds = to_device(a0), to_device(t0, split_tokens=128), to_device(s0, split_tokens=256)
+    assert ta.launch_info(ds.shape)["mode"] == "two_launch"
+    ws = torch.zeros(max(ta.workspace_size(d.shape) for d in (da, dt, ds)),
                      dtype=torch.uint8, device="cuda")
-    da.workspace = dt.workspace = ws
+    da.workspace = dt.workspace = ds.workspace = ws
     oa1, la1 = torch.empty_like(da.q), torch.empty(da.q.shape[:2], device="cuda")
     oa2, la2 = torch.empty_like(da.q), torch.empty(da.q.shape[:2], device="cuda")
     ot, lt = torch.empty_like(dt.q), torch.empty(dt.q.shape[:2], device="cuda")
+    os_, ls_ = torch.empty_like(ds.q), torch.empty(ds.q.shape[:2], device="cuda")
 
     def calls(stream):
         ta.workspace_init(ws, stream=stream)
-        for d, o, l in ((da, oa1, la1), (dt, ot, lt), (da, oa2, la2)):
+        for d, o, l in ((da, oa1, la1), (dt, ot, lt), (da, oa2, la2), (ds, os_, ls_)):
             ta.verify(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
                       d.k_tree, d.v_tree, d.parents, d.tree_offsets, ws, out=o, lse=l,
                       stream=stream)
@@ -168,9 +176,10 @@ def test_verify_graph_capture_replay():
         calls(side)
     torch.cuda.synchronize()
     for rep, (sa, st) in enumerate(((201, 211), (202, 212), (203, 213))):
-        a, t = _same_shape_inputs(sa), _ticket_inputs(st)
+        a, t, o1 = _same_shape_inputs(sa), _ticket_inputs(st), _one_seq_inputs(221 + rep)
         _copy_inputs(da, to_device(a))
         _copy_inputs(dt, to_device(t, split_tokens=128))
+        _copy_inputs(ds, to_device(o1, split_tokens=256))
         torch.cuda.synchronize()
         say(f"graph: replay {rep}")
         g.replay()
@@ -178,6 +187,7 @@ def test_verify_graph_capture_replay():
         assert ta.get_error(ws) == 0
         _check(a, oa1, la1, f"replay {rep} first call")
         _check(t, ot, lt, f"replay {rep} ticket call")
+        _check(o1, os_, ls_, f"replay {rep} two-launch call")
         assert torch.equal(oa1, oa2) and torch.equal(la1, la2)
         # eager work on the same workspace between replays
         oe, le = run_verify(dt)
