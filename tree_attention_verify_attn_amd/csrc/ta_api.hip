@@ -350,6 +350,7 @@ int launch_combine(const Params& p, hipStream_t stream) {
   constexpr int QMAX = kMaxSplits / NSLOT;
   int qg = 1;
   while (qg * QMAX < p.s_max) qg <<= 1;
+  if (qg > NSLOT) return kErrUnsupported;  // more chunks than kMaxSplits (the chunk choice prevents it)
   const int rows = p.total_nodes * p.group;
   const int rp = cdiv(rows, kRowsPerPass);
   const int wpg = cdiv(rows < kRowsPerPass ? rows : kRowsPerPass, NSLOT / qg);
