@@ -1189,7 +1189,8 @@ __device__ __forceinline__ void process_item(const Params& p, unsigned char* rin
     if (with_tree && !big) {
       raw_barrier();  // staged rows of every wave and the mask words are in LDS
       // a key part past the tree's last node sees no key of the tree block
-      // (config 4's tree chunk, the launch's slowest: 12.65 to 12.54 us)
+      // (on the 8k verify with one KV head and 5 query heads the tree chunk
+      // is the launch's slowest: 12.65 to 12.54 us a call)
       if constexpr (decltype(act_tag)::value)
         if (kp * decltype(ks_tag)::value < si.T)
           compute(std::true_type{}, ks_tag, std::true_type{}, tk, tv, 0, 0);
