@@ -1,0 +1,81 @@
+"""A seeded sweep of random shapes through the fused verify and the prefix
+pass, each against the fp64 oracle: batch sizes, GQA groupings, head dims,
+dtypes, ragged prefix lengths (empty ones included), trees of 1-256 nodes
+and forests, caller chunk sizes and a max_prefix_len above the actual
+lengths.  Together they reach every launch mode (first round with the
+meeting, two launches, the device-chosen chunk, tickets with the solo
+combine) in combinations the hand-picked cases do not.  The case's
+parameters are printed before its GPU step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, assert_close_lse, host, run_verify, say, to_device, tolerances
+from helpers import random_tree
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+MAX_MACS = 6e8  # oracle work per case: sum over sequences of T x Hq x (P + T) x D
+
+
+def _case(k):
+    rng = np.random.default_rng(7000 + k)
+    dtype = "bf16" if rng.random() < 0.7 else "f32"
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 5, 8]))
+    while Hkv * G > 64:
+        G //= 2
+    Hq = Hkv * G
+    B = 1 if rng.random() < 0.4 else int(rng.integers(2, 49))
+    tmax = int(rng.choice([4, 12, 12, 64, 100, 256], p=[0.2, 0.3, 0.2, 0.1, 0.1, 0.1]))
+    trees = [random_tree(rng, int(rng.integers(1, tmax + 1)), forest_p=0.05 if rng.random() < 0.2 else 0.0)
+             for _ in range(B)]
+    lens = []
+    for _ in range(B):
+        u = rng.random()
+        lens.append(0 if u < 0.08 else int(rng.integers(1, 64)) if u < 0.2 else int(rng.integers(64, 6000)))
+    # keep the oracle's work bounded: shorten prefixes until it fits
+    def macs():
+        return sum(len(t) * Hq * (p + len(t)) * D for t, p in zip(trees, lens))
+    while macs() > MAX_MACS and any(lens):
+        lens = [p // 2 for p in lens]
+    while macs() > MAX_MACS and len(trees) > 1:  # large trees alone: fewer sequences
+        trees, lens = trees[:-1], lens[:-1]
+    B = len(trees)
+    split = int(rng.choice([0, 0, 0, 64, 128, 320, 1024]))
+    extra = int(rng.integers(5, 40)) if rng.random() < 0.2 else 0
+    inp = make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, prefix_lens=lens,
+                      trees=trees, rng=rng, seed=7000 + k, name=f"random{k}", permute_blocks=True,
+                      spare_blocks=int(rng.integers(0, 5)), extra_table_cols=extra)
+    max_p = None
+    if extra:
+        max_p = min(inp.max_blocks_per_seq * 64, max(inp.max_prefix_len, 1) + 64 * extra // 2)
+    return inp, split, max_p
+
+
+@pytest.mark.parametrize("k", range(N_CASES))
+def test_random_shape_against_oracle(k):
+    import tree_attention_verify_attn_amd as ta
+    inp, split, max_p = _case(k)
+    d = to_device(inp, split_tokens=split, max_prefix_len=max_p)
+    info = ta.launch_info(d.shape)
+    say(f"random shape {k}: {inp.dtype} B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
+        f"D={inp.head_dim} trees<={inp.max_tree_nodes} P<={inp.max_prefix_len} "
+        f"max_prefix_len={d.shape.max_prefix_len} split={split}: {info}")
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(out), o_want, tol_o, f"random {k} o")
+    assert_close_lse(host(lse), l_want, tol_l, f"random {k} lse")
+    po, pl = ta.prefix(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
+                       d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    wpo, wpl = oracle.prefix_only(inp)
+    assert_close(host(po), wpo, tol_o, f"random {k} prefix o")
+    assert_close_lse(host(pl), wpl, tol_l, f"random {k} prefix lse")
