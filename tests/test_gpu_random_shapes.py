@@ -13,7 +13,7 @@ import torch
 import oracle
 from gpu_util import assert_close, assert_close_lse, host, run_verify, say, to_device, tolerances
 from helpers import random_tree
-from workloads import make_inputs
+from workloads import make_inputs, place_tree_in_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +21,8 @@ N_CASES = 64
 MAX_MACS = 6e8  # oracle work per case: sum over sequences of T x Hq x (P + T) x D
 
 
-def _case(k):
-    rng = np.random.default_rng(7000 + k)
+def _case(k, incache=False):
+    rng = np.random.default_rng((9000 if incache else 7000) + k)
     dtype = "bf16" if rng.random() < 0.7 else "f32"
     D = int(rng.choice([64, 128]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
@@ -48,12 +48,20 @@ def _case(k):
     B = len(trees)
     split = int(rng.choice([0, 0, 0, 64, 128, 320, 1024]))
     extra = int(rng.integers(5, 40)) if rng.random() < 0.2 else 0
+    spare = int(rng.integers(0, 5))
+    if incache:   # room in every table row and in the pool for a tree region
+        extra, spare = max(extra, 5), spare + 5 * B + 2
     inp = make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, prefix_lens=lens,
                       trees=trees, rng=rng, seed=7000 + k, name=f"random{k}", permute_blocks=True,
-                      spare_blocks=int(rng.integers(0, 5)), extra_table_cols=extra)
+                      spare_blocks=spare, extra_table_cols=extra)
     max_p = None
-    if extra:
+    if extra and not incache:
         max_p = min(inp.max_blocks_per_seq * 64, max(inp.max_prefix_len, 1) + 64 * extra // 2)
+    elif extra > 5:   # in-cache: the bound leaves room for the tree region
+        max_p = min(inp.max_blocks_per_seq * 64 - 64 * 5, max(inp.max_prefix_len, 1) + 64 * extra // 2)
+        max_p = max(max_p, inp.max_prefix_len)
+    if incache:
+        inp, _ = place_tree_in_cache(inp, rng)
     return inp, split, max_p
 
 
@@ -79,3 +87,26 @@ def test_random_shape_against_oracle(k):
     wpo, wpl = oracle.prefix_only(inp)
     assert_close(host(po), wpo, tol_o, f"random {k} prefix o")
     assert_close_lse(host(pl), wpl, tol_l, f"random {k} prefix lse")
+
+
+N_INCACHE = 24
+
+
+@pytest.mark.parametrize("k", range(N_INCACHE))
+def test_random_incache_against_oracle(k):
+    """The same kind of sweep with each tree's K/V rows in the paged cache
+    right after its prefix (tree_attn_verify_incache)."""
+    import tree_attention_verify_attn_amd as ta
+    ic, split, max_p = _case(k, incache=True)
+    d = to_device(ic, split_tokens=split, max_prefix_len=max_p)
+    say(f"random in-cache shape {k}: {ic.dtype} B={ic.batch} Hq={ic.num_q_heads} Hkv={ic.num_kv_heads} "
+        f"D={ic.head_dim} trees<={ic.max_tree_nodes} P<={ic.max_prefix_len} "
+        f"max_prefix_len={d.shape.max_prefix_len} split={split}")
+    out, lse = ta.verify_incache(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
+                                 d.parents, d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    o_want, l_want, _ = oracle.verify_incache(ic)
+    tol_o, tol_l = tolerances(ic)
+    assert_close(host(out), o_want, tol_o, f"random in-cache {k} o")
+    assert_close_lse(host(lse), l_want, tol_l, f"random in-cache {k} lse")
