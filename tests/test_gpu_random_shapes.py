@@ -1,5 +1,6 @@
-"""A seeded sweep of random shapes through the fused verify and the prefix
-pass, each against the fp64 oracle: batch sizes, GQA groupings, head dims,
+"""A seeded sweep of random shapes through the fused verify and the split
+path (mask words bit for bit, prefix pass, suffix pass, merge), each against
+the fp64 oracle: batch sizes, GQA groupings, head dims,
 dtypes, ragged prefix lengths (empty ones included), trees of 1-256 nodes
 and forests, caller chunk sizes and a max_prefix_len above the actual
 lengths.  Together they reach every launch mode (first round with the
@@ -11,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, assert_close_lse, host, run_verify, say, to_device, tolerances
+from gpu_util import (assert_close, assert_close_lse, host, run_split, run_verify, say, to_device,
+                      tolerances)
 from helpers import random_tree
 from workloads import make_inputs, place_tree_in_cache
 
@@ -65,6 +67,12 @@ def _case(k, incache=False):
     return inp, split, max_p
 
 
+def _split(d):
+    import tree_attention_verify_attn_amd as ta
+    out, lse, (po, pl, so, sl, mask) = run_split(d)
+    return so, sl, out, lse, mask
+
+
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_random_shape_against_oracle(k):
     import tree_attention_verify_attn_amd as ta
@@ -87,6 +95,16 @@ def test_random_shape_against_oracle(k):
     wpo, wpl = oracle.prefix_only(inp)
     assert_close(host(po), wpo, tol_o, f"random {k} prefix o")
     assert_close_lse(host(pl), wpl, tol_l, f"random {k} prefix lse")
+    # the split path: mask words bit for bit, the suffix pass and the merged result
+    so_, sl_, mo, ml, mask = _split(d)
+    W = -(-d.shape.max_tree_nodes // 64)
+    np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64).reshape(-1, W),
+                                  oracle.build_masks_words(inp, W).reshape(-1, W))
+    wso, wsl = oracle.suffix_only(inp)
+    assert_close(host(so_), wso, tol_o, f"random {k} suffix o")
+    assert_close_lse(host(sl_), wsl, tol_l, f"random {k} suffix lse")
+    assert_close(host(mo), o_want, tol_o, f"random {k} split o")
+    assert_close_lse(host(ml), l_want, tol_l, f"random {k} split lse")
 
 
 N_INCACHE = 24
