@@ -216,12 +216,34 @@ def _dist(durs) -> dict:
             "p90_us": round(q[8], 3), "min_us": round(min(durs), 3), "max_us": round(max(durs), 3)}
 
 
-def floor_run(torch, nbytes: int, steps: int, replica_bytes: float) -> dict:
+def kv_tiles(inp):
+    """Byte offsets of the paged K and V tiles a verify call reads, in the order
+    the attention kernel streams them (sequence, KV head, block; K then V),
+    within one buffer holding the K pool and then the V pool; and the tile and
+    pool sizes."""
+    import numpy as np
+    Hkv, D = inp.num_kv_heads, inp.head_dim
+    tile = 64 * D * inp.elem_bytes
+    pool = inp.num_blocks * Hkv * tile
+    parts = []
+    for b in range(inp.batch):
+        nb = -(-int(inp.prefix_lens[b]) // 64)
+        ids = inp.block_table[b, :nb].astype(np.int64)
+        for g in range(Hkv):
+            k = (ids * Hkv + g) * tile
+            parts.append(np.stack([k, k + pool], axis=1).reshape(-1))
+    offs = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    return offs, tile, pool
+
+
+def floor_run(torch, nbytes: int, steps: int, replica_bytes: float, inp=None) -> dict:
     """Reference floors for a launch that streams `nbytes` from HBM, timed like
     the benchmark (rotating replicas of at least `replica_bytes` in total so
     every step reads HBM, the GPU held while the host queues the K steps, one
     event pair around them): a device-wide sum of the bytes (read only), a
-    device copy of them (read + write), and a one-workgroup empty launch."""
+    device copy of them (read + write), a one-workgroup empty launch, the
+    measurement library's plain streaming read of the bytes, and (with the
+    workload's inputs) its gather read of the paged K/V tiles the call reads."""
     n = nbytes // 2
     R = max(1, math.ceil(replica_bytes / nbytes))
     src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(R)]
@@ -268,7 +290,35 @@ def floor_run(torch, nbytes: int, steps: int, replica_bytes: float) -> dict:
               "4096x512x4": (4096, 512, 4), "2048x256x8": (2048, 256, 8)}
     sr = {k: round(stream_read(*v), 3) for k, v in shapes.items()}
     best = min(sr, key=sr.get)
-    return {"floor_bytes": 2 * n, "replicas": R, "steps": steps,
+    gather = {}
+    if inp is not None:
+        import numpy as np
+        offs, tile, pool = kv_tiles(inp)
+        del src, dst
+        Rg = max(1, math.ceil(replica_bytes / (2 * pool)))
+        pools = [torch.empty(2 * pool, dtype=torch.uint8, device="cuda") for _ in range(Rg)]
+        d_offs = torch.from_numpy(np.ascontiguousarray(offs)).cuda()
+        gbytes = len(offs) * tile
+
+        def gather_read(grid, threads, loads):
+            def fn(r):
+                rc = lib.ta_floor_gather(ctypes.c_void_p(pools[r % Rg].data_ptr()),
+                                         ctypes.c_void_p(d_offs.data_ptr()), len(offs), tile, grid,
+                                         threads, loads, ctypes.c_void_p(sink.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"ta_floor_gather failed ({rc})")
+            return timed(fn)
+
+        gshapes = {k: v for k, v in (("256x512x4", (256, 512, 4)), ("1024x512x4", (1024, 512, 4)),
+                                     ("2048x256x8", (2048, 256, 8)))
+                   if -(-len(offs) // v[0]) <= 4096}
+        gr = {k: round(gather_read(*v), 3) for k, v in gshapes.items()}
+        gbest = min(gr, key=gr.get)
+        gather = {"gather_tiles": len(offs), "gather_tile_bytes": tile, "gather_bytes": gbytes,
+                  "gather_replicas": Rg, "gather_read_us": gr, "gather_read_best_us": gr[gbest],
+                  "gather_read_best_shape": gbest,
+                  "gather_read_best_GBps": round(gbytes / gr[gbest] / 1e3, 1)}
+    return {"floor_bytes": 2 * n, "replicas": R, "steps": steps, **gather,
             "stream_read_bytes": nb16,
             "stream_read_us": sr,
             "stream_read_best_us": sr[best], "stream_read_best_shape": best,
@@ -289,6 +339,10 @@ def floor_lib():
     lib.ta_floor_read.restype = ctypes.c_int
     lib.ta_floor_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ta_floor_gather.restype = ctypes.c_int
+    lib.ta_floor_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
     return lib
 
 
@@ -486,7 +540,7 @@ def main() -> int:
     log(f"building workload cfg{args.config}")
     inp = make_config(args.config)
     if args.floor:
-        res = floor_run(torch, algorithmic_bytes(inp), args.steps, args.replica_bytes)
+        res = floor_run(torch, algorithmic_bytes(inp), args.steps, args.replica_bytes, inp)
         res["workload"] = CONFIG_NAMES[args.config]
         print(json.dumps(res), flush=True)
         return 0

@@ -3,7 +3,8 @@
  * ta_floor_read streams `bytes` from device memory at `src` and does nothing
  * else, so its time per launch is the floor for any kernel that has to read
  * the same bytes once (the benchmark's floor mode times it beside the
- * attention kernel over the same algorithmic bytes).
+ * attention kernel over the same algorithmic bytes); ta_floor_gather (below)
+ * does the same for a list of tiles, the paged layout of a KV cache.
  *
  *   src      device pointer, 16-byte aligned; read only.
  *   bytes    a positive multiple of 16.
@@ -35,6 +36,17 @@ extern "C" {
 
 int ta_floor_read(const void* src, size_t bytes, int grid, int threads, int loads, unsigned* sink,
                   hipStream_t stream);
+
+/* ta_floor_gather reads `ntiles` tiles of `tile_bytes` each (a positive
+ * multiple of 16, at most 16 MiB), tile k at byte offset tile_offsets[k] from
+ * `base` (device pointers; base and every offset 16-byte aligned, every tile
+ * inside the caller's allocation), the way the attention kernel reads paged
+ * K/V tiles.  Workgroup i takes tiles [i * per, (i + 1) * per), per =
+ * ceil(ntiles / grid) <= 4096, in list order; sink word i receives the XOR of
+ * every 32-bit word of its tiles.  grid, threads, loads and the return codes
+ * as ta_floor_read. */
+int ta_floor_gather(const void* base, const long long* tile_offsets, int ntiles, size_t tile_bytes,
+                    int grid, int threads, int loads, unsigned* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

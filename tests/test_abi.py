@@ -197,10 +197,32 @@ def floor_lib():
     return lib
 
 
-def test_floor_library_exports_its_header_symbol():
+def test_floor_library_exports_its_header_symbols():
     names = re.findall(r"\b(ta_floor_\w+)\s*\(", open(FLOOR_HEADER).read())
-    assert names == ["ta_floor_read"]
-    assert hasattr(floor_lib(), "ta_floor_read")
+    assert sorted(set(names)) == ["ta_floor_gather", "ta_floor_read"]
+    for n in names:
+        assert hasattr(floor_lib(), n)
+
+
+@pytest.mark.parametrize("args", [
+    (None, FAKE, 4, 1024, 8, 256, 4),          # null base
+    (FAKE, None, 4, 1024, 8, 256, 4),          # null tile list
+    (FAKE, FAKE, 0, 1024, 8, 256, 4),          # no tiles
+    (FAKE, FAKE, 4, 1000, 8, 256, 4),          # tile not a multiple of 16
+    (FAKE, FAKE, 4, 48, 8, 256, 4),            # 3 words a tile: not a power of two
+    (FAKE + 8, FAKE, 4, 1024, 8, 256, 4),      # misaligned base
+    (FAKE, FAKE, 5000, 1024, 1, 256, 4),       # more than 4096 tiles a workgroup
+    (FAKE, FAKE, 4, 1024, 8, 96, 4),           # threads not a multiple of 64
+    (FAKE, FAKE, 4, 1024, 8, 256, 3),          # unsupported loads in flight
+])
+def test_floor_gather_rejects_bad_arguments(args):
+    lib = floor_lib()
+    lib.ta_floor_gather.restype = ctypes.c_int
+    lib.ta_floor_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    base, offs, n, tb, grid, threads, loads = args
+    assert lib.ta_floor_gather(base, offs, n, tb, grid, threads, loads, FAKE, None) == 1
 
 
 @pytest.mark.parametrize("args", [

@@ -41,3 +41,40 @@ def test_stream_read_covers_every_word(nbytes, grid, threads, loads):
         if len(share):
             want[i] = np.bitwise_xor.reduce(share.reshape(-1))
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("ntiles,tile_bytes,grid,threads,loads", [
+    (1, 16, 1, 64, 2),
+    (300, 1024, 7, 192, 4),          # ragged last share
+    (2048, 16384, 256, 512, 4),      # the 8k verify's K/V tiles, one workgroup per CU
+    (100, 4096, 300, 256, 8),        # more workgroups than tiles: empty shares
+])
+def test_gather_read_covers_every_tile(ntiles, tile_bytes, grid, threads, loads):
+    say(f"floor gather tiles={ntiles} tile_bytes={tile_bytes} grid={grid} threads={threads} loads={loads}")
+    rng = np.random.default_rng(ntiles ^ tile_bytes)
+    pool_tiles = ntiles + 17
+    words = rng.integers(0, 2**32, size=pool_tiles * tile_bytes // 4, dtype=np.uint64).astype(np.uint32)
+    order = rng.permutation(pool_tiles)[:ntiles].astype(np.int64)
+    offs = order * tile_bytes
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    d_offs = torch.from_numpy(offs).cuda()
+    sink = torch.full((grid,), -1, dtype=torch.int32, device="cuda")
+    lib = floor_lib()
+    lib.ta_floor_gather.restype = ctypes.c_int
+    lib.ta_floor_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    rc = lib.ta_floor_gather(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(d_offs.data_ptr()),
+                             ntiles, tile_bytes, grid, threads, loads, ctypes.c_void_p(sink.data_ptr()),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    got = sink.cpu().numpy().view(np.uint32)
+    tiles = words.reshape(pool_tiles, tile_bytes // 4)
+    per = -(-ntiles // grid)
+    want = np.zeros(grid, dtype=np.uint32)
+    for i in range(grid):
+        sel = order[i * per:(i + 1) * per]
+        if len(sel):
+            want[i] = np.bitwise_xor.reduce(tiles[sel].reshape(-1))
+    np.testing.assert_array_equal(got, want)
