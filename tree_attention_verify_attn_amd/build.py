@@ -29,6 +29,9 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels whose leading arguments are scalars get them in SGPRs with the
+    # dispatch (at most 16 dwords) instead of by a load at entry
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -347,16 +347,17 @@ int launch_combine(const Params& p, hipStream_t stream) {
   const int st = launch_status();
   if (st != kOk) return st;
   constexpr int NSLOT = kAttnThreads / (D / 4);
-  constexpr int QMAX = kMaxSplits / NSLOT;
-  int qg = 1;
-  while (qg * QMAX < p.s_max) qg <<= 1;
+  const int qg = combine_qg<D>(p.s_max);
   if (qg > NSLOT) return kErrUnsupported;  // more chunks than kMaxSplits (the chunk choice prevents it)
   const int rows = p.total_nodes * p.group;
   const int rp = cdiv(rows, kRowsPerPass);
-  const int wpg = cdiv(rows < kRowsPerPass ? rows : kRowsPerPass, NSLOT / qg);
+  const int wpg = combine_wpg<D>(rows, qg);
   using OutT = typename std::conditional<FUSED, T, float>::type;
+  // scalar arguments only: the first 14 dwords arrive preloaded in SGPRs
   hipLaunchKernelGGL((combine_kernel<OutT, D>), dim3(unsigned(p.hkv * rp * wpg)),
-                     dim3(kAttnThreads), 0, stream, p, wpg, qg);
+                     dim3(kAttnThreads), 0, stream, static_cast<const float*>(p.partials),
+                     p.prefix_lens, static_cast<OutT*>(p.out), p.lse_out, p.s_max, p.group,
+                     p.total_nodes, p.rows_slot, p.hq, p.max_prefix, p.chunk);
   return launch_status();
 }
 

@@ -116,6 +116,23 @@ struct WsLayout {
 };
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// combine_kernel's launch shape, computed alike by the host and the kernel:
+// NSLOT row slots of D / 4 lanes per workgroup; QG row slots share one row
+// (the fewest, a power of two, whose QMAX partial loads per lane cover the S
+// chunks), so a workgroup takes NSLOT / QG rows and a group of R rows (at
+// most kRowsPerPass) needs wpg workgroups.
+template <int D>
+__host__ __device__ inline int combine_qg(int S) {
+  constexpr int QMAX = kMaxSplits / (kAttnThreads / (D / 4));
+  int qg = 1;
+  while (qg * QMAX < S) qg <<= 1;
+  return qg;
+}
+template <int D>
+__host__ __device__ inline int combine_wpg(int rows, int qg) {
+  return cdiv(rows < kRowsPerPass ? rows : kRowsPerPass, kAttnThreads / (D / 4) / qg);
+}
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace ta

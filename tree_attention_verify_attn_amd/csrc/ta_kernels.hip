@@ -1630,8 +1630,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(Params p) {
 // slots split its S partials between them, QMAX loads per lane, all issued
 // up front; the QG slots then meet in LDS.  OutT: the output element type
 // (the shape's dtype for the fused verify, fp32 for the prefix pass).
+// Plain scalar arguments rather than Params: the library is built with
+// kernarg preloading, so they reach the SGPRs with the dispatch and the
+// partial loads leave without waiting on a kernarg load.
 template <typename OutT, int D>
-__global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg, int QG) {
+__global__ void __launch_bounds__(kAttnThreads)
+combine_kernel(const float* __restrict__ partials, const int* __restrict__ prefix_lens,
+               OutT* __restrict__ out, float* __restrict__ lse_out, int S, int G,
+               int total_nodes, int rows_slot, int hq, int max_prefix, int chunk) {
   constexpr int L4 = D / 4;
   constexpr int NSLOT = kAttnThreads / L4;
   constexpr int QMAX = kMaxSplits / NSLOT;  // QG * QMAX >= S for S <= kMaxSplits
@@ -1639,9 +1645,10 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
   __shared__ float red_l[NSLOT];
   __shared__ __attribute__((aligned(16))) float red_o[NSLOT * D];
   const int tid = threadIdx.x;
-  const int S = p.s_max;
-  const int G = p.group;
-  const int R = p.total_nodes * G;
+  const int QG = combine_qg<D>(S);
+  const int R = total_nodes * G;
+  const int wpg = combine_wpg<D>(R, QG);
+  const int slot_floats = rows_slot * (D + 2);  // fp32 o rows, then m and l per row
   const int RP = cdiv(R, kRowsPerPass);
   const int t = int(blockIdx.x) / wpg;
   const int rp = t % RP;
@@ -1654,22 +1661,22 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
   const int rb = rs / QG;
   const int r = (int(blockIdx.x) % wpg) * (NSLOT / QG) + rb;
   const bool valid = r < rcount;
-  const float* g0 = p.partials + size_t(t) * size_t(S) * p.slot_floats;  // chunk 0's slot
-  const uint32_t gbytes = uint32_t(S) * uint32_t(p.slot_floats) * 4u;
-  const int moff = p.rows_slot * D;
-  const int loff = moff + p.rows_slot;
+  const float* g0 = partials + size_t(t) * size_t(S) * slot_floats;  // chunk 0's slot
+  const uint32_t gbytes = uint32_t(S) * uint32_t(slot_floats) * 4u;
+  const int moff = rows_slot * D;
+  const int loff = moff + rows_slot;
   // The grid was sized from max_prefix_len; the actual prefix length, read in
   // the same trip as the partials, says which chunks ran: chunks past it
   // stored nothing this call (their slots hold older data), and with a single
   // chunk the attention kernel wrote the output rows itself.
-  const int p_read = p.prefix_lens[0];
+  const int p_read = prefix_lens[0];
   float mq[QMAX], lq[QMAX];
   float4 oq[QMAX];
 #pragma unroll
   for (int j = 0; j < QMAX; ++j) {
     const int q = qg + QG * j;
     if (valid && q < S) {
-      const uint32_t so = uint32_t(q * p.slot_floats);
+      const uint32_t so = uint32_t(q * slot_floats);
       mq[j] = coherent_load4(g0, gbytes, (so + moff + r) * 4u);
       lq[j] = coherent_load4(g0, gbytes, (so + loff + r) * 4u);
       oq[j] = coherent_load16(g0, gbytes, (so + r * D + 4 * d4) * 4u);
@@ -1679,8 +1686,8 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
       oq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  const int P = p_read >= 0 && p_read <= p.max_prefix ? p_read : 0;  // as attn_kernel reads it
-  const int s_run = P > 0 ? cdiv(P, p.chunk) : 1;
+  const int P = p_read >= 0 && p_read <= max_prefix ? p_read : 0;  // as attn_kernel reads it
+  const int s_run = P > 0 ? cdiv(P, chunk) : 1;
 #pragma unroll
   for (int j = 0; j < QMAX; ++j)
     if (qg + QG * j >= s_run) {
@@ -1736,8 +1743,8 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
     o = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int rr = rlo + r;
-  const size_t orow = size_t(rr / G) * p.hq + g * G + rr % G;
-  OutT* dst = static_cast<OutT*>(p.out) + orow * D + 4 * d4;
+  const size_t orow = size_t(rr / G) * hq + g * G + rr % G;
+  OutT* dst = out + orow * D + 4 * d4;
   if constexpr (sizeof(OutT) == 2) {
     const uint32_t lo = uint32_t(f32_to_bf16(o.x)) | (uint32_t(f32_to_bf16(o.y)) << 16);
     const uint32_t hi = uint32_t(f32_to_bf16(o.z)) | (uint32_t(f32_to_bf16(o.w)) << 16);
@@ -1745,7 +1752,7 @@ __global__ void __launch_bounds__(kAttnThreads) combine_kernel(Params p, int wpg
   } else {
     *reinterpret_cast<float4*>(dst) = o;
   }
-  if (d4 == 0 && p.lse_out) p.lse_out[orow] = lse;
+  if (d4 == 0 && lse_out) lse_out[orow] = lse;
 }
 
 // ============================================================ mask kernel
