@@ -179,6 +179,23 @@ def test_launch_info_mode_choice():
     # a batch whose groups fit the grid: the kernel picks the chunk from the actual lengths
     i = ta.launch_info(shape(batch=32, num_q_heads=8, num_kv_heads=1, total_tree_nodes=128))
     assert i["mode"] == "device"
+    # short prefixes stream in one chunk per sequence: one sequence up to 3
+    # blocks (one launch, no exchange), from 4 blocks two launches again
+    for P, mode in ((1, "first_round"), (150, "first_round"), (192, "first_round"),
+                    (193, "two_launch"), (256, "two_launch")):
+        i = ta.launch_info(shape(max_prefix_len=P, max_blocks_per_seq=8))
+        assert i["mode"] == mode, (P, i)
+        if mode == "first_round":
+            assert i["split_tokens"] == 64 * -(-P // 64) and i["max_items"] == 8, (P, i)
+    # a batch up to 6 blocks: one chunk per sequence, chosen by the host (one
+    # workgroup per group); from 7 blocks the kernel picks the chunk (and
+    # still takes one chunk a sequence when the actual lengths are that short)
+    i = ta.launch_info(shape(batch=8, max_prefix_len=384, max_blocks_per_seq=6,
+                             total_tree_nodes=96))
+    assert i["split_tokens"] == 384 and i["mode"] == "first_round" and i["max_items"] == 64
+    i = ta.launch_info(shape(batch=8, max_prefix_len=385, max_blocks_per_seq=7,
+                             total_tree_nodes=96))
+    assert i["split_tokens"] < 385 and i["mode"] == "device"
     with pytest.raises(ta.TreeAttnError):
         ta.launch_info(shape(head_dim=96))
     assert load().tree_attn_launch_info(ctypes.byref(shape()), None) == 1

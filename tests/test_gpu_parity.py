@@ -278,6 +278,63 @@ def test_verify_split_sizes(split):
     _check_verify(inp, out, lse, f"cfg4 split {split}")
 
 
+def _batch(seed, *, dtype, Hq, Hkv, D, lens, extra_cols=0, trees=None):
+    rng = np.random.default_rng(seed)
+    return make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       prefix_lens=list(lens), trees=trees or [TREE_12] * len(lens), rng=rng,
+                       seed=seed, name=f"batch{seed}", permute_blocks=True, spare_blocks=3,
+                       extra_table_cols=extra_cols)
+
+
+# Short prefixes stream in one chunk per sequence (no exchange): one sequence
+# up to 3 blocks, a batch whose max_prefix_len is up to 6 blocks (the host's
+# chunk), a batch whose longest actual prefix is up to 6 blocks (the kernel
+# picks that chunk even when max_prefix_len would allow more), and the first
+# lengths past each bound, which split again.
+SHORT_CASES = [
+    ("one-seq-150", lambda: _one_seq(520, dtype="bf16", Hq=8, Hkv=2, D=128, P=150), None,
+     "first_round"),
+    ("one-seq-192-f32-d64", lambda: _one_seq(521, dtype="f32", Hq=4, Hkv=1, D=64, P=192), None,
+     "first_round"),
+    ("one-seq-193", lambda: _one_seq(522, dtype="bf16", Hq=5, Hkv=1, D=128, P=193), None,
+     "two_launch"),
+    ("batch8-up-to-384", lambda: _batch(523, dtype="bf16", Hq=8, Hkv=2, D=128,
+                                        lens=(384, 1, 0, 200, 321, 64, 65, 383), extra_cols=58),
+     4096, "device"),
+    ("batch4-host-chunk", lambda: _batch(526, dtype="bf16", Hq=32, Hkv=8, D=128,
+                                         lens=(300, 5, 384, 0)), None, "first_round"),
+    ("batch6-385", lambda: small_inputs(524, dtype="bf16", B=6, Hq=8, Hkv=1, D=128,
+                                        prefix_lens=(385, 17, 130, 384, 0, 256),
+                                        trees=[[-1, 0, 1, 2]] * 6), None, "device"),
+    ("batch5-d64-f32", lambda: _batch(525, dtype="f32", Hq=4, Hkv=2, D=64,
+                                      lens=(100, 300, 5, 64, 250), extra_cols=27), 2048, "device"),
+]
+
+
+@pytest.mark.parametrize("name,make,max_p,mode", SHORT_CASES, ids=[c[0] for c in SHORT_CASES])
+def test_verify_short_prefixes_one_chunk(name, make, max_p, mode):
+    import tree_attention_verify_attn_amd as ta
+    inp = make()
+    d = to_device(inp, max_prefix_len=max_p)
+    info = ta.launch_info(d.shape)
+    say(f"verify short prefixes {name}: {info}")
+    assert info["mode"] == mode, info
+    out, lse = run_verify(d)
+    assert ta.get_error(d.workspace) == 0
+    _check_verify(inp, out, lse, f"short {name}")
+    out2, lse2 = run_verify(d)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # the prefix pass alone makes the same chunk choice
+    po, pl = ta.prefix(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
+                       d.tree_offsets, d.workspace)
+    torch.cuda.synchronize()
+    assert ta.get_error(d.workspace) == 0
+    wpo, wpl = oracle.prefix_only(inp)
+    tol_o, tol_l = tolerances(inp)
+    assert_close(host(po), wpo, tol_o, f"short {name} o_prefix")
+    assert_close_lse(host(pl), wpl, tol_l, f"short {name} lse_prefix")
+
+
 EDGE_CASES = [
     ("empty-prefix", lambda: small_inputs(80, dtype="bf16", B=3, Hq=4, Hkv=2, D=128,
                                           prefix_lens=(0, 0, 0))),

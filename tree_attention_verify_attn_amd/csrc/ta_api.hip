@@ -190,8 +190,11 @@ int choose_chunk(const ta_shape* s, bool fused) {
   const int max_splits = cap < kMaxSplits ? cap : kMaxSplits;
   const int min_chunk = kBlock * cdiv(cdiv(P, max_splits), kBlock);
   int chunk;
+  const int nb = cdiv(P, kBlock);
   if (s->split_tokens > 0) {
     chunk = s->split_tokens;
+  } else if (nb <= (one_sequence(s) ? kOneChunkBlocks : kOneChunkBlocksBatch)) {
+    chunk = nb * kBlock;  // short prefixes: one chunk, no exchange
   } else {
     const int G = group_of(s);
     const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
@@ -212,7 +215,12 @@ int choose_chunk(const ta_shape* s, bool fused) {
 
 // The kernel picks the chunk from the actual prefix lengths unless the caller
 // fixed it or the launch numbers items without a table.
-bool chunk_auto(const ta_shape* s) { return s->split_tokens == 0 && !one_sequence(s); }
+bool chunk_auto(const ta_shape* s) {
+  // (up to kOneChunkBlocksBatch blocks the host's chunk is already one chunk
+  // per sequence, and the launch needs only a workgroup per group)
+  return s->split_tokens == 0 && !one_sequence(s) &&
+         cdiv(s->max_prefix_len, kBlock) > kOneChunkBlocksBatch;
+}
 
 // Item slots a launch may use beyond groups x chunks-per-group: with the
 // kernel's own chunk every item fits in the grid's first round.

@@ -20,6 +20,12 @@ constexpr int kMaxSplits = 64;    // cap on work items per (sequence, head, row 
 // One-sequence launches whose groups have at least this many chunks end the
 // attention kernel at the partial stores and combine in a second launch.
 constexpr int kTwoLaunchMinChunks = 2;
+// Short prefixes stream in one chunk per sequence, with no exchange at all:
+// one sequence up to this many blocks (against two launches of 64-token
+// chunks), a batch whose longest prefix has up to kOneChunkBlocksBatch
+// (against chunks that meet in the launch).
+constexpr int kOneChunkBlocks = 3;
+constexpr int kOneChunkBlocksBatch = 6;
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 constexpr int kMaxRingSlots = 2;       // KV blocks the attention kernel keeps in LDS

@@ -153,12 +153,6 @@ __device__ __forceinline__ void block_sum2_max(int& a, int& b, int& c, int* scra
   __syncthreads();
 }
 
-// When the host leaves the chunk to the kernel (p.chunk_auto) and the groups
-// (sequence, KV head, row pass) are fewer than the grid's workgroups, the
-// chunk comes from the actual prefix lengths: the smallest multiple of 64
-// tokens with which every item fits in the first round (the sum of the
-// groups' chunk counts stays within the grid) and no group has more than
-// kMaxSplits chunks.  `chunk` returns the chunk in force.
 // Ascending bitonic sort of np keys (np a power of two, np <= kMaxBatch);
 // element i = q * kAttnThreads + thread lives in keys[q] of that thread.
 // Partners less than a wave apart meet by lane shuffles, partners in other
@@ -207,6 +201,15 @@ __device__ void bitonic_sort(int (&keys)[kSortSlots], int np, int* xbuf) {
     }
 }
 
+// When the host leaves the chunk to the kernel (p.chunk_auto), the chunk
+// comes from the actual prefix lengths.  If the longest has at most
+// kOneChunkBlocksBatch blocks, every sequence streams in one chunk (its
+// chunks would cost more to meet than to stream); otherwise, if the groups
+// (sequence, KV head, row pass) are fewer than the grid's workgroups, the
+// chunk is the smallest multiple of 64 tokens with which every item fits in
+// the first round (the sum of the groups' chunk counts stays within the
+// grid) and no group has more than kMaxSplits chunks.  `chunk` returns the
+// chunk in force.
 __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* perm, int* scratch,
                            int* xbuf, int& chunk) {
   const int tid = threadIdx.x;
@@ -240,7 +243,9 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
   chunk = p.chunk;
   if (p.chunk_auto) {
     block_sum2_max(work, groups, max_blocks, scratch);
-    if (groups < p.first_round) {
+    if (max_blocks <= kOneChunkBlocksBatch) {
+      chunk = max(max_blocks, 1) * kBlock;  // short prefixes: one chunk each, no exchange
+    } else if (groups < p.first_round) {
       int cb = max(cdiv(work, p.first_round - groups), cdiv(max_blocks, kMaxSplits));
       cb = min(max(cb, 1), kMaxChunk / kBlock);
       chunk = cb * kBlock;
