@@ -335,6 +335,33 @@ def test_verify_short_prefixes_one_chunk(name, make, max_p, mode):
     assert_close_lse(host(pl), wpl, tol_l, f"short {name} lse_prefix")
 
 
+# The log-sum-exp output is optional (lse_out = NULL): every way a row's
+# output is written -- by the one chunk of its group, by a chunk after the
+# meeting in the launch, by the last arrival in ticket mode, by the combine
+# kernel of a two-launch call -- must then write o alone, the same bits.
+NO_LSE_CASES = [
+    ("one-chunk", lambda: make_config(1), 0),
+    ("two-launch", lambda: _one_seq(530, dtype="bf16", Hq=8, Hkv=2, D=128, P=1500), 256),
+    ("meeting", lambda: small_inputs(531, dtype="bf16", B=6, Hq=8, Hkv=2, D=128,
+                                     prefix_lens=(900, 64, 1500, 0, 700, 1200)), 256),
+    ("ticket", lambda: _ticket_inputs(532, B=40, lens=np.random.default_rng(532).integers(321, 2049, 40)),
+     64),
+]
+
+
+@pytest.mark.parametrize("name,make,split", NO_LSE_CASES, ids=[c[0] for c in NO_LSE_CASES])
+def test_verify_without_lse_output(name, make, split):
+    import tree_attention_verify_attn_amd as ta
+    inp = make()
+    d = to_device(inp, split_tokens=split)
+    say(f"verify without lse {name}: {ta.launch_info(d.shape)}")
+    out, lse = run_verify(d)
+    out2, lse2 = run_verify(d, want_lse=False)
+    assert lse2 is None and ta.get_error(d.workspace) == 0
+    assert torch.equal(out, out2)
+    _check_verify(inp, out2, lse, f"no lse {name}")
+
+
 EDGE_CASES = [
     ("empty-prefix", lambda: small_inputs(80, dtype="bf16", B=3, Hq=4, Hkv=2, D=128,
                                           prefix_lens=(0, 0, 0))),
