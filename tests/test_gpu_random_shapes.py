@@ -23,8 +23,8 @@ N_CASES = 64
 MAX_MACS = 6e8  # oracle work per case: sum over sequences of T x Hq x (P + T) x D
 
 
-def _case(k, incache=False):
-    rng = np.random.default_rng((9000 if incache else 7000) + k)
+def _case(k, incache=False, short=False):
+    rng = np.random.default_rng((9000 if incache else 11000 if short else 7000) + k)
     dtype = "bf16" if rng.random() < 0.7 else "f32"
     D = int(rng.choice([64, 128]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
@@ -37,9 +37,14 @@ def _case(k, incache=False):
     trees = [random_tree(rng, int(rng.integers(1, tmax + 1)), forest_p=0.05 if rng.random() < 0.2 else 0.0)
              for _ in range(B)]
     lens = []
+    # short: up to 3, 6 or 7 blocks (one chunk per sequence, and past the bounds)
+    ub = int(rng.choice([192, 384, 448])) if short else 0
     for _ in range(B):
         u = rng.random()
-        lens.append(0 if u < 0.08 else int(rng.integers(1, 64)) if u < 0.2 else int(rng.integers(64, 6000)))
+        if short:
+            lens.append(0 if u < 0.1 else int(rng.integers(1, ub + 1)))
+        else:
+            lens.append(0 if u < 0.08 else int(rng.integers(1, 64)) if u < 0.2 else int(rng.integers(64, 6000)))
     # keep the oracle's work bounded: shorten prefixes until it fits
     def macs():
         return sum(len(t) * Hq * (p + len(t)) * D for t, p in zip(trees, lens))
@@ -48,13 +53,14 @@ def _case(k, incache=False):
     while macs() > MAX_MACS and len(trees) > 1:  # large trees alone: fewer sequences
         trees, lens = trees[:-1], lens[:-1]
     B = len(trees)
-    split = int(rng.choice([0, 0, 0, 64, 128, 320, 1024]))
-    extra = int(rng.integers(5, 40)) if rng.random() < 0.2 else 0
+    split = 0 if short else int(rng.choice([0, 0, 0, 64, 128, 320, 1024]))
+    extra = int(rng.integers(5, 40)) if rng.random() < (0.4 if short else 0.2) else 0
     spare = int(rng.integers(0, 5))
     if incache:   # room in every table row and in the pool for a tree region
         extra, spare = max(extra, 5), spare + 5 * B + 2
     inp = make_inputs(dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, prefix_lens=lens,
-                      trees=trees, rng=rng, seed=7000 + k, name=f"random{k}", permute_blocks=True,
+                      trees=trees, rng=rng, seed=(11000 if short else 7000) + k,
+                      name=f"random{k}", permute_blocks=True,
                       spare_blocks=spare, extra_table_cols=extra)
     max_p = None
     if extra and not incache:
@@ -75,36 +81,53 @@ def _split(d):
 
 @pytest.mark.parametrize("k", range(N_CASES))
 def test_random_shape_against_oracle(k):
-    import tree_attention_verify_attn_amd as ta
     inp, split, max_p = _case(k)
+    _check_case(f"random {k}", inp, split, max_p)
+
+
+N_SHORT = 24
+
+
+@pytest.mark.parametrize("k", range(N_SHORT))
+def test_random_short_prefixes_against_oracle(k):
+    """Prefixes of at most 7 blocks and the library's own chunk: one chunk per
+    sequence (chosen by the host from max_prefix_len, or by the kernel from
+    the actual lengths when max_prefix_len is larger) or, past the bounds,
+    split as before."""
+    inp, split, max_p = _case(k, short=True)
+    _check_case(f"random short {k}", inp, split, max_p)
+
+
+def _check_case(k, inp, split, max_p):
+    import tree_attention_verify_attn_amd as ta
     d = to_device(inp, split_tokens=split, max_prefix_len=max_p)
     info = ta.launch_info(d.shape)
-    say(f"random shape {k}: {inp.dtype} B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
+    say(f"{k}: {inp.dtype} B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
         f"D={inp.head_dim} trees<={inp.max_tree_nodes} P<={inp.max_prefix_len} "
         f"max_prefix_len={d.shape.max_prefix_len} split={split}: {info}")
     out, lse = run_verify(d)
     assert ta.get_error(d.workspace) == 0
     o_want, l_want, _ = oracle.verify(inp)
     tol_o, tol_l = tolerances(inp)
-    assert_close(host(out), o_want, tol_o, f"random {k} o")
-    assert_close_lse(host(lse), l_want, tol_l, f"random {k} lse")
+    assert_close(host(out), o_want, tol_o, f"{k} o")
+    assert_close_lse(host(lse), l_want, tol_l, f"{k} lse")
     po, pl = ta.prefix(d.shape, d.q, d.k_cache, d.v_cache, d.block_table, d.prefix_lens,
                        d.tree_offsets, d.workspace)
     torch.cuda.synchronize()
     assert ta.get_error(d.workspace) == 0
     wpo, wpl = oracle.prefix_only(inp)
-    assert_close(host(po), wpo, tol_o, f"random {k} prefix o")
-    assert_close_lse(host(pl), wpl, tol_l, f"random {k} prefix lse")
+    assert_close(host(po), wpo, tol_o, f"{k} prefix o")
+    assert_close_lse(host(pl), wpl, tol_l, f"{k} prefix lse")
     # the split path: mask words bit for bit, the suffix pass and the merged result
     so_, sl_, mo, ml, mask = _split(d)
     W = -(-d.shape.max_tree_nodes // 64)
     np.testing.assert_array_equal(mask.cpu().numpy().view(np.uint64).reshape(-1, W),
                                   oracle.build_masks_words(inp, W).reshape(-1, W))
     wso, wsl = oracle.suffix_only(inp)
-    assert_close(host(so_), wso, tol_o, f"random {k} suffix o")
-    assert_close_lse(host(sl_), wsl, tol_l, f"random {k} suffix lse")
-    assert_close(host(mo), o_want, tol_o, f"random {k} split o")
-    assert_close_lse(host(ml), l_want, tol_l, f"random {k} split lse")
+    assert_close(host(so_), wso, tol_o, f"{k} suffix o")
+    assert_close_lse(host(sl_), wsl, tol_l, f"{k} suffix lse")
+    assert_close(host(mo), o_want, tol_o, f"{k} split o")
+    assert_close_lse(host(ml), l_want, tol_l, f"{k} split lse")
 
 
 N_INCACHE = 24
