@@ -235,7 +235,7 @@ WsLayout layout_for(const ta_shape* s, int chunk, int min_item_slots = 0) {
   int rows = s->max_tree_nodes * G;
   if (rows > kRowsPerPass) rows = kRowsPerPass;
   L.rows_slot = 16 * cdiv(rows, 16);
-  L.slot_floats = L.rows_slot * (D + 2);  // fp32 o rows, then m and l per row
+  L.slot_floats = slot_floats_of(L.rows_slot, D);
   L.num_groups = s->batch * s->num_kv_heads * L.rp_max;
   L.s_max = s->max_prefix_len > 0 ? cdiv(s->max_prefix_len, chunk) : 1;
   // large batches: dense per-XCD numbering from a prefix table; small: static

@@ -123,6 +123,10 @@ struct WsLayout {
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Floats per chunk-partial slot: rows_slot fp32 o rows of D, then the running
+// max m and sum l of every row.
+__host__ __device__ inline int slot_floats_of(int rows_slot, int D) { return rows_slot * (D + 2); }
+
 // combine_kernel's launch shape, computed alike by the host and the kernel:
 // NSLOT row slots of D / 4 lanes per workgroup; QG row slots share one row
 // (the fewest, a power of two, whose QMAX partial loads per lane cover the S

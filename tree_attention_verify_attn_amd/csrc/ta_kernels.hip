@@ -1657,7 +1657,7 @@ combine_kernel(const float* __restrict__ partials, const int* __restrict__ prefi
   const int QG = combine_qg<D>(S);
   const int R = total_nodes * G;
   const int wpg = combine_wpg<D>(R, QG);
-  const int slot_floats = rows_slot * (D + 2);  // fp32 o rows, then m and l per row
+  const int slot_floats = slot_floats_of(rows_slot, D);
   const int RP = cdiv(R, kRowsPerPass);
   const int t = int(blockIdx.x) / wpg;
   const int rp = t % RP;
