@@ -116,7 +116,8 @@ typedef struct {
   int32_t num_blocks;         /* pool size: valid block ids are [0, num_blocks) */
   int32_t split_tokens;       /* prefix tokens per work item: 0 = library heuristic
                                  (short prefixes in one chunk per sequence: up to
-                                 3 blocks for one sequence, 6 for a batch),
+                                 3 blocks for one sequence, 6 for a batch, 8 for
+                                 a batch of 32 groups or more),
                                  else a positive multiple of 64 */
   float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim) */
   ta_dtype dtype;             /* element type of q, caches, tree K/V and out */
@@ -336,7 +337,8 @@ int32_t tree_attn_split_tokens(const ta_shape* shape);
  *   info[0]  prefix tokens per work item (a multiple of 64; the kernel may
  *            pick another from the actual prefix lengths when info[3] is 2
  *            and split_tokens is 0: one chunk per sequence if the longest
- *            has at most 6 blocks, else the smallest that fits the grid)
+ *            has at most 6 blocks (8 with 32 groups of sequence, KV head and
+ *            row pass or more), else the smallest that fits the grid)
  *   info[1]  workgroups of the launch (one per CU at most)
  *   info[2]  bound on the work items (workspace partial slots)
  *   info[3]  0: every item runs in the first round and the chunks of a group

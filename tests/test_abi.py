@@ -187,15 +187,22 @@ def test_launch_info_mode_choice():
         assert i["mode"] == mode, (P, i)
         if mode == "first_round":
             assert i["split_tokens"] == 64 * -(-P // 64) and i["max_items"] == 8, (P, i)
-    # a batch up to 6 blocks: one chunk per sequence, chosen by the host (one
-    # workgroup per group); from 7 blocks the kernel picks the chunk (and
-    # still takes one chunk a sequence when the actual lengths are that short)
+    # a batch up to 6 blocks (8 with 32 groups or more): one chunk per
+    # sequence, chosen by the host (one workgroup per group); past that the
+    # kernel picks the chunk (and still takes one chunk a sequence when the
+    # actual lengths are that short)
     i = ta.launch_info(shape(batch=8, max_prefix_len=384, max_blocks_per_seq=6,
-                             total_tree_nodes=96))
-    assert i["split_tokens"] == 384 and i["mode"] == "first_round" and i["max_items"] == 64
+                             total_tree_nodes=96, num_q_heads=8, num_kv_heads=1))
+    assert i["split_tokens"] == 384 and i["mode"] == "first_round" and i["max_items"] == 16  # 2 row passes
     i = ta.launch_info(shape(batch=8, max_prefix_len=385, max_blocks_per_seq=7,
-                             total_tree_nodes=96))
+                             total_tree_nodes=96, num_q_heads=8, num_kv_heads=1))
     assert i["split_tokens"] < 385 and i["mode"] == "device"
+    i = ta.launch_info(shape(batch=8, max_prefix_len=512, max_blocks_per_seq=8,
+                             total_tree_nodes=96))  # 64 groups
+    assert i["split_tokens"] == 512 and i["mode"] == "first_round" and i["max_items"] == 64
+    i = ta.launch_info(shape(batch=8, max_prefix_len=513, max_blocks_per_seq=9,
+                             total_tree_nodes=96))
+    assert i["split_tokens"] < 513 and i["mode"] == "device"
     with pytest.raises(ta.TreeAttnError):
         ta.launch_info(shape(head_dim=96))
     assert load().tree_attn_launch_info(ctypes.byref(shape()), None) == 1

@@ -287,10 +287,10 @@ def _batch(seed, *, dtype, Hq, Hkv, D, lens, extra_cols=0, trees=None):
 
 
 # Short prefixes stream in one chunk per sequence (no exchange): one sequence
-# up to 3 blocks, a batch whose max_prefix_len is up to 6 blocks (the host's
-# chunk), a batch whose longest actual prefix is up to 6 blocks (the kernel
-# picks that chunk even when max_prefix_len would allow more), and the first
-# lengths past each bound, which split again.
+# up to 3 blocks, a batch whose max_prefix_len is up to 6 blocks, or 8 with
+# 32 groups or more (the host's chunk), a batch whose longest actual prefix
+# is that short (the kernel picks that chunk even when max_prefix_len would
+# allow more), and the first lengths past each bound, which split again.
 SHORT_CASES = [
     ("one-seq-150", lambda: _one_seq(520, dtype="bf16", Hq=8, Hkv=2, D=128, P=150), None,
      "first_round"),
@@ -303,6 +303,12 @@ SHORT_CASES = [
      4096, "device"),
     ("batch4-host-chunk", lambda: _batch(526, dtype="bf16", Hq=32, Hkv=8, D=128,
                                          lens=(300, 5, 384, 0)), None, "first_round"),
+    ("batch8-wide-8-blocks", lambda: _batch(527, dtype="bf16", Hq=32, Hkv=8, D=128,
+                                            lens=(512, 449, 300, 0, 65, 500, 480, 1)),
+     None, "first_round"),
+    ("batch8-wide-kernel", lambda: _batch(528, dtype="bf16", Hq=32, Hkv=8, D=64,
+                                          lens=(450, 10, 511, 200, 0, 64, 300, 129), extra_cols=56),
+     4096, "device"),
     ("batch6-385", lambda: small_inputs(524, dtype="bf16", B=6, Hq=8, Hkv=1, D=128,
                                         prefix_lens=(385, 17, 130, 384, 0, 256),
                                         trees=[[-1, 0, 1, 2]] * 6), None, "device"),

@@ -191,14 +191,14 @@ int choose_chunk(const ta_shape* s, bool fused) {
   const int min_chunk = kBlock * cdiv(cdiv(P, max_splits), kBlock);
   int chunk;
   const int nb = cdiv(P, kBlock);
+  const int G = group_of(s);
+  const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
+                           cdiv(s->max_tree_nodes * G, kRowsPerPass);
   if (s->split_tokens > 0) {
     chunk = s->split_tokens;
-  } else if (nb <= (one_sequence(s) ? kOneChunkBlocks : kOneChunkBlocksBatch)) {
+  } else if (one_sequence(s) ? nb <= kOneChunkBlocks : one_chunk_batch(nb, groups)) {
     chunk = nb * kBlock;  // short prefixes: one chunk, no exchange
   } else {
-    const int G = group_of(s);
-    const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
-                             cdiv(s->max_tree_nodes * G, kRowsPerPass);
     // one sequence: fill about four fifths of the grid rather than all of it.
     // Fewer, longer chunks stream no slower (the CUs share the HBM) and
     // shrink the partial exchange: the 8k verify with 8 KV heads runs 208
@@ -216,10 +216,12 @@ int choose_chunk(const ta_shape* s, bool fused) {
 // The kernel picks the chunk from the actual prefix lengths unless the caller
 // fixed it or the launch numbers items without a table.
 bool chunk_auto(const ta_shape* s) {
-  // (up to kOneChunkBlocksBatch blocks the host's chunk is already one chunk
-  // per sequence, and the launch needs only a workgroup per group)
+  // (where the host's chunk is already one chunk per sequence, the launch
+  // needs only a workgroup per group)
+  const long long groups = static_cast<long long>(s->batch) * s->num_kv_heads *
+                           cdiv(s->max_tree_nodes * group_of(s), kRowsPerPass);
   return s->split_tokens == 0 && !one_sequence(s) &&
-         cdiv(s->max_prefix_len, kBlock) > kOneChunkBlocksBatch;
+         !one_chunk_batch(cdiv(s->max_prefix_len, kBlock), groups);
 }
 
 // Item slots a launch may use beyond groups x chunks-per-group: with the

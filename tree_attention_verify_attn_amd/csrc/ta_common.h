@@ -23,9 +23,13 @@ constexpr int kTwoLaunchMinChunks = 2;
 // Short prefixes stream in one chunk per sequence, with no exchange at all:
 // one sequence up to this many blocks (against two launches of 64-token
 // chunks), a batch whose longest prefix has up to kOneChunkBlocksBatch
-// (against chunks that meet in the launch).
+// (against chunks that meet in the launch), or up to kOneChunkBlocksWide
+// when at least kOneChunkWideGroups groups (sequence, KV head, row pass)
+// share the launch and splitting would add many meetings.
 constexpr int kOneChunkBlocks = 3;
 constexpr int kOneChunkBlocksBatch = 6;
+constexpr int kOneChunkBlocksWide = 8;
+constexpr int kOneChunkWideGroups = 32;
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU (gfx950)
 constexpr int kMaxRingSlots = 2;       // KV blocks the attention kernel keeps in LDS
@@ -122,6 +126,13 @@ struct WsLayout {
 };
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// A batch whose longest prefix has `blocks` blocks, over `groups` groups,
+// streams every sequence in one chunk.
+__host__ __device__ inline bool one_chunk_batch(int blocks, long long groups) {
+  return blocks <= kOneChunkBlocksBatch ||
+         (blocks <= kOneChunkBlocksWide && groups >= kOneChunkWideGroups);
+}
 
 // Floats per chunk-partial slot: rows_slot fp32 o rows of D, then the running
 // max m and sum l of every row.

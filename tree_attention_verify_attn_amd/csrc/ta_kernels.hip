@@ -202,9 +202,10 @@ __device__ void bitonic_sort(int (&keys)[kSortSlots], int np, int* xbuf) {
 }
 
 // When the host leaves the chunk to the kernel (p.chunk_auto), the chunk
-// comes from the actual prefix lengths.  If the longest has at most
-// kOneChunkBlocksBatch blocks, every sequence streams in one chunk (its
-// chunks would cost more to meet than to stream); otherwise, if the groups
+// comes from the actual prefix lengths.  If the longest is short enough
+// (one_chunk_batch: up to 6 blocks, or 8 with 32 groups or more), every
+// sequence streams in one chunk (its chunks would cost more to meet than to
+// stream); otherwise, if the groups
 // (sequence, KV head, row pass) are fewer than the grid's workgroups, the
 // chunk is the smallest multiple of 64 tokens with which every item fits in
 // the first round (the sum of the groups' chunk counts stays within the
@@ -243,7 +244,7 @@ __device__ int build_table(const Params& p, int* cum, int* ot, int* pl, int* per
   chunk = p.chunk;
   if (p.chunk_auto) {
     block_sum2_max(work, groups, max_blocks, scratch);
-    if (max_blocks <= kOneChunkBlocksBatch) {
+    if (one_chunk_batch(max_blocks, groups)) {
       chunk = max(max_blocks, 1) * kBlock;  // short prefixes: one chunk each, no exchange
     } else if (groups < p.first_round) {
       int cb = max(cdiv(work, p.first_round - groups), cdiv(max_blocks, kMaxSplits));
